@@ -1,0 +1,263 @@
+"""Seeded synthetic inputs for batch attention over a paged KV cache.
+
+This module only *builds inputs*: request lengths, a flat page table, a
+page pool and query rows.  It holds none of the attention arithmetic, and it
+is the one module that both the CPU oracle's tests and the GPU path's tests
+and benchmark draw their inputs from.
+
+Layouts (FlashInfer 0.2 release blog, "flexible block sparsity and vector
+sparsity"; flashinfer-trace discussion #15, "Notes on fa3_gqa_prefill_v1"):
+
+* ``q``        bf16 ``[total_q, Hq, D]``, ragged by ``qo_indptr[B+1]``;
+* ``paged_kv`` bf16 ``[num_pages, 2, page_size, Hkv, D]`` (NHD; index 0 = K,
+  1 = V);
+* flat page table ``kv_indptr[B+1]`` (offsets into ``kv_indices``),
+  ``kv_indices[nnz]`` (page ids), ``kv_last_page_len[B]`` (valid slots in each
+  request's last page);
+* ragged dense K/V ``k, v`` bf16 ``[total_kv, Hkv, D]`` with token offsets
+  ``kv_token_indptr[B+1]`` (only built where the workload asks for it).
+
+Every random draw uses ``torch.Generator('cpu').manual_seed(seed)`` in a fixed
+order: lengths -> page permutation -> Q -> K/V -> poison.  Values are fp32
+N(0, 1) rounded to bf16.  Large tensors are drawn in fixed-size chunks so that
+host memory stays bounded; the chunk size is part of the recipe.
+
+Unused pool pages and the slots past ``kv_last_page_len`` in each last page are
+filled with NaN ("poison") wherever the workload enables it: a kernel that reads
+a slot it must not read turns its output into NaN.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+from typing import Optional
+
+import torch
+
+# Fixed chunk (elements) for drawing large normal tensors; part of the recipe.
+_DRAW_CHUNK = 1 << 24
+
+
+@dataclass
+class Workload:
+    name: str
+    seed: int
+    batch: int
+    num_qo_heads: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    causal: bool
+    sm_scale: float
+    qo_lens: list
+    kv_lens: list
+    qo_indptr: torch.Tensor          # int32 [B+1]
+    kv_indptr: torch.Tensor          # int32 [B+1] (pages)
+    kv_indices: torch.Tensor         # int32 [nnz]
+    kv_last_page_len: torch.Tensor   # int32 [B]
+    num_pages: int
+    q: torch.Tensor                  # bf16 [total_q, Hq, D]
+    paged_kv: torch.Tensor           # bf16 [num_pages, 2, ps, Hkv, D]
+    k: Optional[torch.Tensor] = None  # bf16 [total_kv, Hkv, D] (ragged dense)
+    v: Optional[torch.Tensor] = None
+    kv_token_indptr: Optional[torch.Tensor] = None  # int32 [B+1]
+    poisoned: bool = False
+    notes: dict = field(default_factory=dict)
+
+    @property
+    def total_q(self) -> int:
+        return int(self.qo_indptr[-1])
+
+    @property
+    def nnz_pages(self) -> int:
+        return int(self.kv_indptr[-1])
+
+
+def _randn_bf16(shape, gen) -> torch.Tensor:
+    """fp32 N(0,1) draws rounded to bf16, drawn in fixed-size chunks."""
+    n = 1
+    for s in shape:
+        n *= int(s)
+    out = torch.empty(n, dtype=torch.bfloat16)
+    pos = 0
+    while pos < n:
+        m = min(_DRAW_CHUNK, n - pos)
+        out[pos:pos + m] = torch.randn(m, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+        pos += m
+    return out.view(*shape)
+
+
+def page_table_for(kv_lens, page_size, num_pages, gen):
+    """Build a flat page table for the given KV lengths.
+
+    Pages are assigned in request order from one random permutation of the
+    pool: ``perm[:nnz]`` in order, so request r owns
+    ``kv_indices[kv_indptr[r]:kv_indptr[r+1]]``.
+    Returns (kv_indptr, kv_indices, kv_last_page_len).
+    """
+    npages = [(L + page_size - 1) // page_size for L in kv_lens]
+    last = [0 if L == 0 else L - (n - 1) * page_size for L, n in zip(kv_lens, npages)]
+    indptr = [0]
+    for n in npages:
+        indptr.append(indptr[-1] + n)
+    nnz = indptr[-1]
+    assert nnz <= num_pages
+    perm = torch.randperm(num_pages, generator=gen)
+    kv_indices = perm[:nnz].to(torch.int32).contiguous()
+    return (torch.tensor(indptr, dtype=torch.int32), kv_indices,
+            torch.tensor(last, dtype=torch.int32))
+
+
+def _poison(paged_kv, kv_indptr, kv_indices, kv_last_page_len, page_size):
+    """NaN-fill every pool slot the page table does not reference."""
+    num_pages = paged_kv.shape[0]
+    used = torch.zeros(num_pages, dtype=torch.bool)
+    used[kv_indices.long()] = True
+    paged_kv[~used] = float("nan")
+    B = kv_last_page_len.numel()
+    for r in range(B):
+        a, b = int(kv_indptr[r]), int(kv_indptr[r + 1])
+        if b > a:
+            last_page = int(kv_indices[b - 1])
+            n = int(kv_last_page_len[r])
+            if n < page_size:
+                paged_kv[last_page, :, n:] = float("nan")
+
+
+def build(name, seed, qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim,
+          page_size, causal=True, pool_slack=0.0, poison=True, ragged=False,
+          gen=None, notes=None, num_pages=None) -> Workload:
+    """Assemble a workload from explicit lengths.
+
+    Draw order after the lengths: page permutation -> Q -> K/V -> poison.
+    With ``ragged=True`` the K/V values are drawn once as dense ragged
+    ``k, v`` tensors and scattered into the pool through the page table, so
+    the dense and the paged form hold identical values.
+    """
+    gen = gen if gen is not None else torch.Generator("cpu").manual_seed(seed)
+    B = len(qo_lens)
+    assert len(kv_lens) == B
+    ps = page_size
+    nnz = sum((L + ps - 1) // ps for L in kv_lens)
+    if num_pages is None:
+        num_pages = max(1, nnz + int(math.ceil(nnz * pool_slack)))
+    num_pages = max(num_pages, nnz, 1)
+    kv_indptr, kv_indices, last = page_table_for(kv_lens, ps, num_pages, gen)
+    qo_indptr = torch.tensor([0] + list(torch.tensor(qo_lens).cumsum(0).tolist()),
+                             dtype=torch.int32)
+    total_q = int(qo_indptr[-1])
+    H, Hk, D = num_qo_heads, num_kv_heads, head_dim
+    q = _randn_bf16((total_q, H, D), gen)
+    k = v = kv_tok = None
+    if ragged:
+        total_kv = sum(kv_lens)
+        kv_tok = torch.tensor([0] + list(torch.tensor(kv_lens).cumsum(0).tolist()),
+                              dtype=torch.int32)
+        k = _randn_bf16((total_kv, Hk, D), gen)
+        v = _randn_bf16((total_kv, Hk, D), gen)
+        paged_kv = torch.zeros((num_pages, 2, ps, Hk, D), dtype=torch.bfloat16)
+        for r in range(B):
+            t0, L = int(kv_tok[r]), kv_lens[r]
+            t = torch.arange(L)
+            page = kv_indices[int(kv_indptr[r]) + t // ps].long()
+            slot = t % ps
+            paged_kv[page, 0, slot] = k[t0:t0 + L]
+            paged_kv[page, 1, slot] = v[t0:t0 + L]
+    else:
+        paged_kv = _randn_bf16((num_pages, 2, ps, Hk, D), gen)
+    if poison:
+        _poison(paged_kv, kv_indptr, kv_indices, last, ps)
+    return Workload(
+        name=name, seed=seed, batch=B, num_qo_heads=H, num_kv_heads=Hk,
+        head_dim=D, page_size=ps, causal=causal, sm_scale=1.0 / math.sqrt(D),
+        qo_lens=list(qo_lens), kv_lens=list(kv_lens), qo_indptr=qo_indptr,
+        kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
+        num_pages=num_pages, q=q, paged_kv=paged_kv, k=k, v=v,
+        kv_token_indptr=kv_tok, poisoned=poison, notes=dict(notes or {}))
+
+
+def _uniform_int(gen, lo, hi, n):
+    """n draws from U{lo..hi} (inclusive)."""
+    return torch.randint(lo, hi + 1, (n,), generator=gen).tolist()
+
+
+# ---------------------------------------------------------------------------
+# The named workloads.  Each takes optional size overrides so that tests can
+# run the same recipe at a size the CPU oracle finishes in seconds.
+# ---------------------------------------------------------------------------
+
+def tiny(seed=1, lens=(17, 33), page_size=4, causal=True, pool_pages=64, **kw) -> Workload:
+    """Causal paged prefill, B=2 with qo_len = kv_len in {17, 33}, Hq=4, Hkv=1,
+    D=64, page_size=4, 64-page pool, partially filled last pages, poisoned."""
+    lens = list(lens)
+    return build("tiny", seed, lens, lens, 4, 1, 64, page_size, causal=causal,
+                 num_pages=pool_pages, **kw)
+
+
+def dense_vs_sparse(seed=2, batch=16, length=1024, heads=32, head_dim=128, **kw) -> Workload:
+    """B requests of L tokens, Hq = Hkv, causal; dense ragged K/V scattered into
+    a page_size=1 pool through a random permutation (vector sparsity)."""
+    lens = [length] * batch
+    return build("dense_vs_sparse", seed, lens, lens, heads, heads, head_dim, 1,
+                 causal=True, ragged=True, poison=kw.pop("poison", False), **kw)
+
+
+def gqa_append(seed=3, batch=32, prefix_range=(512, 8192), chunk_range=(64, 1024),
+               **kw) -> Workload:
+    """Chunked prefill with a prefix: prefix P ~ U{...}, chunk n ~ U{...},
+    qo_len = n, kv_len = P + n, Hq=32, Hkv=8, D=128, page_size=16, pool with
+    10% slack, causal mask offset by the prefix."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    P = _uniform_int(gen, prefix_range[0], prefix_range[1], batch)
+    n = _uniform_int(gen, chunk_range[0], chunk_range[1], batch)
+    return build("gqa_append", seed, n, [a + b for a, b in zip(P, n)],
+                 kw.pop("heads", 32), kw.pop("kv_heads", 8), kw.pop("head_dim", 128),
+                 kw.pop("page_size", 16), causal=True, pool_slack=0.10, gen=gen,
+                 notes={"prefix": P}, **kw)
+
+
+def long_causal(seed=4, batch=2, length=16384, **kw) -> Workload:
+    """B=2 requests of L=16384, Hq=32, Hkv=8, D=128, page_size=16, permuted
+    pages with 10% slack."""
+    lens = [length] * batch
+    return build("long_causal", seed, lens, lens, kw.pop("heads", 32),
+                 kw.pop("kv_heads", 8), kw.pop("head_dim", 128),
+                 kw.pop("page_size", 16), causal=True, pool_slack=0.10,
+                 poison=kw.pop("poison", True), **kw)
+
+
+def batch_decode(seed=5, batch=256, kv_log2_range=(7.0, 15.0), kv_clamp=(128, 32768),
+                 **kw) -> Workload:
+    """B single-token queries, Hq=32, Hkv=8, D=128, page_size=16; kv_len =
+    clamp(round(2^U(a, b)), lo, hi) (log-uniform), permuted pages, 2% slack."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    a, b = kv_log2_range
+    u = torch.rand(batch, generator=gen, dtype=torch.float64) * (b - a) + a
+    kv = [int(min(max(round(2.0 ** float(x)), kv_clamp[0]), kv_clamp[1])) for x in u]
+    return build("batch_decode", seed, [1] * batch, kv, kw.pop("heads", 32),
+                 kw.pop("kv_heads", 8), kw.pop("head_dim", 128),
+                 kw.pop("page_size", 16), causal=kw.pop("causal", True),
+                 pool_slack=0.02, gen=gen, poison=kw.pop("poison", True), **kw)
+
+
+def p5_shape(seed=6, batch=4, max_len=700, **kw) -> Workload:
+    """Hq=16, Hkv=1, D=128, page_size=64, causal prefill with qo = kv ~ U{1..700}
+    (the shape named gqa_paged_prefill_causal_h16_kv1_d128_ps64)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    lens = _uniform_int(gen, 1, max_len, batch)
+    return build("p5_shape", seed, lens, lens, 16, 1, 128, 64, causal=True,
+                 pool_slack=0.25, gen=gen, **kw)
+
+
+WORKLOADS = {
+    "tiny": tiny,
+    "dense_vs_sparse": dense_vs_sparse,
+    "gqa_append": gqa_append,
+    "long_causal": long_causal,
+    "batch_decode": batch_decode,
+    "p5_shape": p5_shape,
+}
+
+
+def make(name: str, **kw) -> Workload:
+    return WORKLOADS[name](**kw)
