@@ -1,0 +1,189 @@
+/*
+ * pka.h - batch attention over a paged KV cache on AMD Instinct MI355X (gfx950).
+ *
+ * The operation (FlashInfer 0.2 release blog, "flexible block sparsity and
+ * vector sparsity"): PageAttention is block-sparse attention whose block
+ * width is page_size; page_size = 1 is per-token (vector) sparsity.  For each
+ * request r of a ragged batch, the query rows q[qo_indptr[r] .. qo_indptr[r+1])
+ * attend over the request's kv_len keys, read through a flat page table
+ * (flashinfer-trace discussion #15, "Notes on fa3_gqa_prefill_v1":
+ * kv_indices + kv_indptr + kv_last_page_len; Q ragged as
+ * [total_q, num_qo_heads, head_dim]).  Every call returns O and a base-2
+ * log-sum-exp (same passage), and states of disjoint KV parts merge into the
+ * state of the whole (FlashInfer documentation, "Attention States and
+ * Recursive Attention", "Merge Attention States").
+ *
+ * Semantics fixed by this library where the pages are silent:
+ *   kv_len      = (npages - 1) * page_size + kv_last_page_len[r], 0 if npages == 0.
+ *   GQA         query head h reads KV head h / (num_qo_heads / num_kv_heads).
+ *   causal      bottom-right: query i sees key j iff j <= i + kv_len - qo_len.
+ *   s_j         = sm_scale * q . k_j,  sm_scale <= 0 selects 1/sqrt(head_dim).
+ *   lse         = log2 sum_j exp(s_j) over the visible keys.
+ *   no key      a row that sees no key gets o = 0 and lse = -inf.
+ *
+ * Layouts (all row-major, contiguous):
+ *   q           bf16 [total_q, num_qo_heads, head_dim]
+ *   paged_kv    bf16 [num_pages, 2, page_size, num_kv_heads, head_dim]  (NHD; 0 = K, 1 = V)
+ *   k, v        bf16 [total_kv, num_kv_heads, head_dim]  (ragged dense form)
+ *   o           bf16 (default) or fp32 (PKA_OUT_FP32) [total_q, num_qo_heads, head_dim]
+ *   lse         fp32 [total_q, num_qo_heads]
+ *
+ * Plan / run split (FlashInfer 0.2 release blog, "faster plan function"): the
+ * plan reads its index arrays from HOST memory, copies what the kernels need
+ * into a caller-owned device workspace with an asynchronous host-to-device
+ * copy on the caller's stream, and never synchronises.  One plan may be run
+ * many times (for instance once per layer) on any q / KV of the planned shape.
+ *
+ * Errors: every int-returning call returns PKA_OK (0) or a PKA_ERR_* code and
+ * records a message readable with pka_last_error() (per thread).  No call
+ * aborts, and no C++ exception crosses this interface.
+ */
+#ifndef PKA_H
+#define PKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+/* A HIP stream (hipStream_t); NULL means the null stream. */
+typedef struct ihipStream_t* pka_stream_t;
+
+/* Opaque plan, owned by the library (pka_plan_destroy frees it). */
+typedef struct pka_plan pka_plan;
+
+enum {
+  PKA_OK = 0,
+  PKA_ERR_INVALID_ARG = 1, /* malformed arrays, null pointers, mismatched plan  */
+  PKA_ERR_UNSUPPORTED = 2, /* head_dim not 64/128, Hq % Hkv != 0, page_size outside [1,128] */
+  PKA_ERR_WORKSPACE = 3,   /* a workspace is smaller than pka_plan_workspace_size asks */
+  PKA_ERR_HIP = 4          /* the HIP runtime reported an error (message has its text)    */
+};
+
+/* Plan flags. */
+#define PKA_DISABLE_SPLIT_KV 0x1u /* never split one request's KV over several work units */
+#define PKA_OUT_FP32 0x2u         /* o is fp32 instead of bf16                               */
+#define PKA_RAGGED_KV 0x4u        /* K/V are ragged dense tensors: kv_indptr counts tokens,
+                                     kv_indices and kv_last_page_len are unused (may be NULL),
+                                     page_size is ignored; run with pka_run_ragged           */
+
+/* Which attention kernel a plan launches. */
+enum { PKA_KERNEL_PREFILL = 0, PKA_KERNEL_DECODE = 1 };
+
+/* Summary of a plan (all counts are exact for the planned batch). */
+typedef struct pka_plan_info {
+  int32_t kernel;           /* PKA_KERNEL_PREFILL or PKA_KERNEL_DECODE                    */
+  int32_t num_units;        /* work units = workgroups of the attention launch             */
+  int32_t num_merge_groups; /* split (request, kv head, row block) groups merged afterwards */
+  int32_t num_partial_rows; /* fp32 partial-state rows held in the float workspace          */
+  int32_t block_rows;       /* packed query rows (token x group head) per work unit         */
+  int32_t kv_chunk;         /* keys per split chunk, 0 when no unit is split                */
+  int32_t batch;
+  int32_t nnz_pages;
+  int64_t total_q;
+  int64_t total_kv;         /* sum of kv_len over the batch                                 */
+  int64_t int_ws_bytes;     /* bytes of the int workspace image the plan uploads            */
+  int64_t float_ws_bytes;   /* bytes of float workspace the runs need                       */
+} pka_plan_info;
+
+/* Message for the last failed call on this thread ("" if none). */
+const char* pka_last_error(void);
+
+/*
+ * Workspace sizes for a plan of this batch.  Pure host call; reads host
+ * arrays qo_indptr[batch+1], kv_indptr[batch+1] and (paged) kv_last_page_len[batch].
+ * Writes the byte counts the two device workspaces of pka_plan_create need.
+ */
+int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_last_page_len, int32_t batch,
+                            int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                            int32_t page_size, int32_t causal, uint32_t flags,
+                            size_t* int_ws_bytes, size_t* float_ws_bytes);
+
+/*
+ * Plan a batch.
+ *   qo_indptr[batch+1], kv_indptr[batch+1], kv_indices[nnz_pages],
+ *   kv_last_page_len[batch]: HOST int32 arrays, read during the call only.
+ *   num_pages_in_pool: pages in paged_kv; every kv_indices entry must lie in
+ *   [0, num_pages_in_pool).  Ids may repeat (shared read-only pages).
+ *   int_ws / float_ws: caller-owned DEVICE buffers of at least the sizes
+ *   pka_plan_workspace_size reports; they must stay valid, and be used by no
+ *   other plan, while this plan is in use.
+ *   stream: the plan's host-to-device copy is enqueued on it; a run on another
+ *   stream must be ordered after it by the caller.
+ *   *out receives a library-owned plan.  The plan owns pinned staging memory
+ *   read by the enqueued copy, so it must outlive that copy.
+ * Validation (PKA_ERR_INVALID_ARG): indptr arrays start at 0 and never
+ * decrease; kv_indptr[batch] == nnz_pages; for a request with pages,
+ * 1 <= kv_last_page_len <= page_size, and 0 when it has none; ids in range.
+ */
+int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                    int32_t batch, int32_t nnz_pages, int32_t num_pages_in_pool,
+                    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                    int32_t page_size, int32_t causal, float sm_scale, uint32_t flags,
+                    void* int_ws, size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes,
+                    pka_stream_t stream, pka_plan** out);
+
+/* Counts and sizes of a plan. */
+int pka_plan_get_info(const pka_plan* plan, pka_plan_info* info);
+
+/*
+ * Host-only planning: the same validation and work decomposition as
+ * pka_plan_create, but the int workspace image is written to host memory
+ * `image` (capacity image_bytes; NULL to query the size through info) instead
+ * of being uploaded.  pka_plan_create uploads exactly these bytes.
+ */
+int pka_plan_host_image(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                        const int32_t* kv_indices, const int32_t* kv_last_page_len,
+                        int32_t batch, int32_t nnz_pages, int32_t num_pages_in_pool,
+                        int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                        int32_t page_size, int32_t causal, uint32_t flags,
+                        void* image, size_t image_bytes, pka_plan_info* info);
+
+/*
+ * Attention over the paged KV cache (plan made without PKA_RAGGED_KV).
+ * q, paged_kv, o, lse: caller-owned DEVICE memory in the layouts above; lse
+ * may be NULL.  Enqueued on `stream` after the plan's copy; returns without
+ * waiting.  The run writes every row of o and lse.
+ */
+int pka_run(const pka_plan* plan, const void* q, const void* paged_kv, void* o, float* lse,
+            pka_stream_t stream);
+
+/* Attention over ragged dense K/V (plan made with PKA_RAGGED_KV). */
+int pka_run_ragged(const pka_plan* plan, const void* q, const void* k, const void* v, void* o,
+                   float* lse, pka_stream_t stream);
+
+/*
+ * Merge attention states (FlashInfer documentation, "Merge Attention States").
+ *   v   fp32 [n, num_states, num_heads, head_dim],  s fp32 [n, num_states, num_heads] (base 2)
+ *   v_out bf16 (default) or fp32 (PKA_OUT_FP32) [n, num_heads, head_dim], s_out fp32 [n, num_heads]
+ * With M = max_s s_s and w_s = 2^(s_s - M): s_out = M + log2 sum_s w_s and
+ * v_out = sum_s w_s v_s / sum_s w_s; states with s = -inf weigh 0, and a row
+ * whose states are all empty gets (0, -inf).  All pointers are device memory;
+ * s_out may be NULL.  head_dim must be a multiple of 4 and at most 1024.
+ */
+int pka_merge_states(const float* v, const float* s, int64_t n, int32_t num_states,
+                     int32_t num_heads, int32_t head_dim, void* v_out, float* s_out,
+                     uint32_t flags, pka_stream_t stream);
+
+/*
+ * Test aid: copy the keys and values the page table selects into dense
+ * k_dense / v_dense bf16 [total_kv, num_kv_heads, head_dim] (requests in
+ * order, each kv_len rows), exactly as the attention kernels address them.
+ */
+int pka_debug_gather(const pka_plan* plan, const void* paged_kv, void* k_dense, void* v_dense,
+                     pka_stream_t stream);
+
+/* Free a plan.  The caller must first make sure the plan's copy and every run
+ * using it have completed (for example by synchronising the stream).  NULL is
+ * a no-op. */
+void pka_plan_destroy(pka_plan* plan);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PKA_H */

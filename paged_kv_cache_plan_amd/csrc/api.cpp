@@ -1,0 +1,362 @@
+// C ABI of the paged-KV attention library (declared in include/pka.h).
+//
+// The plan runs the host planner on host index arrays, stages the resulting
+// int workspace image in pinned host memory owned by the plan, and enqueues
+// one asynchronous host-to-device copy on the caller's stream; it never
+// synchronises (FlashInfer 0.2 release blog, "faster plan function").  Runs
+// only enqueue kernels.  Errors become status codes plus a per-thread message.
+#include <hip/hip_runtime_api.h>
+
+#include <cmath>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <exception>
+#include <string>
+
+#include "../../include/pka.h"
+#include "args.h"
+#include "launch.h"
+#include "planner.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+int hip_error(const char* what, hipError_t e) {
+  return set_error(PKA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
+}
+
+constexpr uint32_t kPlanMagic = 0x4e4c5050u;  // "PPLN"
+constexpr uint32_t kKnownFlags = PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV;
+
+int env_int(const char* name) {
+  const char* s = std::getenv(name);
+  return s ? std::atoi(s) : 0;
+}
+
+}  // namespace
+
+struct pka_plan {
+  uint32_t magic;
+  pka_plan_info info;
+  int32_t num_qo_heads, num_kv_heads, head_dim, page_size, group, causal, num_pages;
+  uint32_t flags;
+  float sm_scale;
+  void* int_ws;
+  void* float_ws;
+  size_t partial_lse_offset;
+  int32_t off_units, off_req, off_merge, off_idx;
+  void* staging;  // pinned copy of the image, read by the enqueued copy
+};
+
+namespace {
+
+pka::PlanInput make_input(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                          const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages,
+                          int32_t num_pages, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
+                          int32_t page_size, int32_t causal, uint32_t flags, bool check_indices) {
+  pka::PlanInput in;
+  in.qo_indptr = qo_indptr;
+  in.kv_indptr = kv_indptr;
+  in.kv_indices = kv_indices;
+  in.kv_last_page_len = kv_last_page_len;
+  in.batch = batch;
+  in.nnz_pages = nnz_pages;
+  in.num_pages = num_pages;
+  in.num_qo_heads = num_qo_heads;
+  in.num_kv_heads = num_kv_heads;
+  in.head_dim = head_dim;
+  in.page_size = page_size;
+  in.causal = causal;
+  in.flags = flags;
+  in.check_indices = check_indices;
+  in.kv_chunk_override = env_int("PKA_KV_CHUNK");
+  return in;
+}
+
+void fill_info(const pka::PlanResult& res, int32_t batch, int32_t nnz, pka_plan_info* info) {
+  info->kernel = res.kernel;
+  info->num_units = res.num_units;
+  info->num_merge_groups = res.num_merge;
+  info->num_partial_rows = res.num_partial_rows;
+  info->block_rows = res.block_rows;
+  info->kv_chunk = res.kv_chunk;
+  info->batch = batch;
+  info->nnz_pages = nnz;
+  info->total_q = res.total_q;
+  info->total_kv = res.total_kv;
+  info->int_ws_bytes = static_cast<int64_t>(res.image.size() * sizeof(int32_t));
+  info->float_ws_bytes = static_cast<int64_t>(res.float_ws_bytes);
+}
+
+int plan_or_error(const pka::PlanInput& in, pka::PlanResult* res) {
+  if (in.flags & ~kKnownFlags) return set_error(PKA_ERR_INVALID_ARG, "unknown flag bits");
+  std::string err;
+  const int st = pka::build_plan(in, res, &err);
+  if (st != pka::kOk) return set_error(st, err);
+  return PKA_OK;
+}
+
+bool plan_ok(const pka_plan* p) { return p && p->magic == kPlanMagic; }
+
+pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const void* v, void* o, float* lse) {
+  pka::AttnArgs a{};
+  const int32_t* iw = static_cast<const int32_t*>(p->int_ws);
+  a.q = static_cast<const uint16_t*>(q);
+  a.k = static_cast<const uint16_t*>(k);
+  a.v = static_cast<const uint16_t*>(v);
+  a.o = o;
+  a.lse = lse;
+  a.part_o = static_cast<float*>(p->float_ws);
+  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(p->float_ws) + p->partial_lse_offset);
+  a.units = iw + p->off_units;
+  a.req = iw + p->off_req;
+  a.kv_indices = iw + p->off_idx;
+  const int64_t row = static_cast<int64_t>(p->num_kv_heads) * p->head_dim;
+  const bool ragged = p->flags & PKA_RAGGED_KV;
+  a.row_stride = static_cast<int32_t>(row);
+  a.page_size = ragged ? 1 : p->page_size;
+  a.v_offset = ragged ? 0 : static_cast<int64_t>(p->page_size) * row;
+  a.page_stride = ragged ? row : 2 * static_cast<int64_t>(p->page_size) * row;
+  int shift = -1;
+  for (int s = 0; s < 8; ++s)
+    if ((1 << s) == a.page_size) shift = s;
+  a.page_shift = shift;
+  a.num_qo_heads = p->num_qo_heads;
+  a.group = p->group;
+  a.out_fp32 = (p->flags & PKA_OUT_FP32) ? 1 : 0;
+  a.scale_log2 = p->sm_scale * 1.4426950408889634f;
+  return a;
+}
+
+int run_common(const pka_plan* p, const void* q, const void* k, const void* v, void* o, float* lse,
+               hipStream_t stream) {
+  if (p->info.total_q == 0) return PKA_OK;
+  if (!q || !o) return set_error(PKA_ERR_INVALID_ARG, "q and o must not be NULL");
+  if (p->info.total_kv > 0 && !k) return set_error(PKA_ERR_INVALID_ARG, "KV pointer must not be NULL");
+  const pka::AttnArgs a = attn_args(p, q, k, v, o, lse);
+  const bool paged = !(p->flags & PKA_RAGGED_KV);
+  hipError_t e;
+  if (p->info.kernel == PKA_KERNEL_DECODE)
+    e = pka::launch_decode(a, p->head_dim, paged, p->info.num_units, stream);
+  else
+    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, p->info.num_units, stream);
+  if (e != hipSuccess) return hip_error("attention launch", e);
+  if (p->info.num_merge_groups > 0) {
+    pka::MergeArgs m{};
+    m.part_o = a.part_o;
+    m.part_lse = a.part_lse;
+    m.groups = static_cast<const int32_t*>(p->int_ws) + p->off_merge;
+    m.req = a.req;
+    m.o = o;
+    m.lse = lse;
+    m.num_qo_heads = p->num_qo_heads;
+    m.group = p->group;
+    m.out_fp32 = a.out_fp32;
+    e = pka::launch_merge(m, p->head_dim, p->info.num_merge_groups, stream);
+    if (e != hipSuccess) return hip_error("merge launch", e);
+  }
+  return PKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* pka_last_error(void) { return g_last_error.c_str(); }
+
+int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
+                            uint32_t flags, size_t* int_ws_bytes, size_t* float_ws_bytes) {
+  try {
+    if (!int_ws_bytes || !float_ws_bytes) return set_error(PKA_ERR_INVALID_ARG, "null size pointer");
+    if (!kv_indptr || batch < 0) return set_error(PKA_ERR_INVALID_ARG, "kv_indptr must not be NULL");
+    const int32_t nnz = kv_indptr[batch];
+    pka::PlanInput in = make_input(qo_indptr, kv_indptr, nullptr, kv_last_page_len, batch, nnz, 0,
+                                   num_qo_heads, num_kv_heads, head_dim, page_size, causal, flags, false);
+    pka::PlanResult res;
+    const int st = plan_or_error(in, &res);
+    if (st != PKA_OK) return st;
+    *int_ws_bytes = res.image.size() * sizeof(int32_t);
+    *float_ws_bytes = res.float_ws_bytes;
+    return PKA_OK;
+  } catch (const std::exception& ex) {
+    return set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
+
+int pka_plan_host_image(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                        const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages,
+                        int32_t num_pages_in_pool, int32_t num_qo_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size, int32_t causal, uint32_t flags, void* image,
+                        size_t image_bytes, pka_plan_info* info) {
+  try {
+    pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
+                                   num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                   causal, flags, true);
+    pka::PlanResult res;
+    const int st = plan_or_error(in, &res);
+    if (st != PKA_OK) return st;
+    if (info) fill_info(res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, info);
+    const size_t need = res.image.size() * sizeof(int32_t);
+    if (image) {
+      if (image_bytes < need) return set_error(PKA_ERR_WORKSPACE, "image buffer too small");
+      std::memcpy(image, res.image.data(), need);
+    }
+    return PKA_OK;
+  } catch (const std::exception& ex) {
+    return set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
+
+int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                    const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages, int32_t num_pages_in_pool,
+                    int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                    int32_t causal, float sm_scale, uint32_t flags, void* int_ws, size_t int_ws_bytes,
+                    void* float_ws, size_t float_ws_bytes, pka_stream_t stream, pka_plan** out) {
+  try {
+    if (!out) return set_error(PKA_ERR_INVALID_ARG, "out must not be NULL");
+    *out = nullptr;
+    if (!int_ws || !float_ws) return set_error(PKA_ERR_INVALID_ARG, "workspaces must not be NULL");
+    if (!std::isfinite(sm_scale)) return set_error(PKA_ERR_INVALID_ARG, "sm_scale must be finite");
+    pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
+                                   num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                   causal, flags, true);
+    pka::PlanResult res;
+    int st = plan_or_error(in, &res);
+    if (st != PKA_OK) return st;
+    const size_t need = res.image.size() * sizeof(int32_t);
+    if (int_ws_bytes < need)
+      return set_error(PKA_ERR_WORKSPACE, "int workspace has " + std::to_string(int_ws_bytes) + " bytes, needs " +
+                                              std::to_string(need));
+    if (float_ws_bytes < res.float_ws_bytes)
+      return set_error(PKA_ERR_WORKSPACE, "float workspace has " + std::to_string(float_ws_bytes) +
+                                              " bytes, needs " + std::to_string(res.float_ws_bytes));
+    pka_plan* p = new pka_plan{};
+    p->magic = kPlanMagic;
+    fill_info(res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, &p->info);
+    p->num_qo_heads = num_qo_heads;
+    p->num_kv_heads = num_kv_heads;
+    p->head_dim = head_dim;
+    p->page_size = page_size;
+    p->group = num_qo_heads / num_kv_heads;
+    p->causal = causal ? 1 : 0;
+    p->num_pages = num_pages_in_pool;
+    p->flags = flags;
+    p->sm_scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
+    p->int_ws = int_ws;
+    p->float_ws = float_ws;
+    p->partial_lse_offset = res.partial_lse_offset;
+    p->off_units = res.image[pka::kHdrOffUnits];
+    p->off_req = res.image[pka::kHdrOffReq];
+    p->off_merge = res.image[pka::kHdrOffMerge];
+    p->off_idx = res.image[pka::kHdrOffIndices];
+    p->staging = nullptr;
+    hipError_t e = hipHostMalloc(&p->staging, need, hipHostMallocDefault);
+    if (e != hipSuccess) {
+      delete p;
+      return hip_error("hipHostMalloc(plan staging)", e);
+    }
+    std::memcpy(p->staging, res.image.data(), need);
+    e = hipMemcpyAsync(int_ws, p->staging, need, hipMemcpyHostToDevice, stream);
+    if (e != hipSuccess) {
+      (void)hipHostFree(p->staging);
+      delete p;
+      return hip_error("hipMemcpyAsync(plan upload)", e);
+    }
+    if (env_int("PKA_LOG"))
+      std::fprintf(stderr, "[pka] plan: %s units=%d merge_groups=%d partial_rows=%d kv_chunk=%d int_ws=%zu float_ws=%zu\n",
+                   res.kernel == pka::kDecode ? "decode" : "prefill", res.num_units, res.num_merge,
+                   res.num_partial_rows, res.kv_chunk, need, res.float_ws_bytes);
+    *out = p;
+    return PKA_OK;
+  } catch (const std::exception& ex) {
+    return set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
+
+int pka_plan_get_info(const pka_plan* plan, pka_plan_info* info) {
+  if (!plan_ok(plan) || !info) return set_error(PKA_ERR_INVALID_ARG, "invalid plan or info pointer");
+  *info = plan->info;
+  return PKA_OK;
+}
+
+int pka_run(const pka_plan* plan, const void* q, const void* paged_kv, void* o, float* lse,
+            pka_stream_t stream) {
+  if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
+  if (plan->flags & PKA_RAGGED_KV)
+    return set_error(PKA_ERR_INVALID_ARG, "plan was made with PKA_RAGGED_KV: use pka_run_ragged");
+  return run_common(plan, q, paged_kv, nullptr, o, lse, stream);
+}
+
+int pka_run_ragged(const pka_plan* plan, const void* q, const void* k, const void* v, void* o, float* lse,
+                   pka_stream_t stream) {
+  if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
+  if (!(plan->flags & PKA_RAGGED_KV))
+    return set_error(PKA_ERR_INVALID_ARG, "plan was made for a paged KV cache: use pka_run");
+  if (plan->info.total_kv > 0 && !v) return set_error(PKA_ERR_INVALID_ARG, "v must not be NULL");
+  return run_common(plan, q, k, v, o, lse, stream);
+}
+
+int pka_merge_states(const float* v, const float* s, int64_t n, int32_t num_states, int32_t num_heads,
+                     int32_t head_dim, void* v_out, float* s_out, uint32_t flags, pka_stream_t stream) {
+  if (n < 0 || num_states < 1 || num_heads < 1 || head_dim < 4 || head_dim % 4 != 0 || head_dim > 1024)
+    return set_error(PKA_ERR_INVALID_ARG, "merge_states: bad sizes");
+  if (flags & ~uint32_t(PKA_OUT_FP32)) return set_error(PKA_ERR_INVALID_ARG, "merge_states: unknown flags");
+  if (n == 0) return PKA_OK;
+  if (!v || !s || !v_out) return set_error(PKA_ERR_INVALID_ARG, "merge_states: null pointer");
+  pka::MergeStatesArgs a{};
+  a.v = v;
+  a.s = s;
+  a.v_out = v_out;
+  a.s_out = s_out;
+  a.n = n;
+  a.num_states = num_states;
+  a.num_heads = num_heads;
+  a.head_dim = head_dim;
+  a.out_fp32 = (flags & PKA_OUT_FP32) ? 1 : 0;
+  const hipError_t e = pka::launch_merge_states(a, stream);
+  if (e != hipSuccess) return hip_error("merge_states launch", e);
+  return PKA_OK;
+}
+
+int pka_debug_gather(const pka_plan* plan, const void* paged_kv, void* k_dense, void* v_dense,
+                     pka_stream_t stream) {
+  if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
+  if (plan->flags & PKA_RAGGED_KV) return set_error(PKA_ERR_INVALID_ARG, "debug_gather needs a paged plan");
+  if (plan->info.total_kv == 0) return PKA_OK;
+  if (!paged_kv || !k_dense || !v_dense) return set_error(PKA_ERR_INVALID_ARG, "null pointer");
+  pka::GatherArgs a{};
+  const int32_t* iw = static_cast<const int32_t*>(plan->int_ws);
+  a.pool = static_cast<const uint16_t*>(paged_kv);
+  a.k_out = static_cast<uint16_t*>(k_dense);
+  a.v_out = static_cast<uint16_t*>(v_dense);
+  a.req = iw + plan->off_req;
+  a.kv_indices = iw + plan->off_idx;
+  const int64_t row = static_cast<int64_t>(plan->num_kv_heads) * plan->head_dim;
+  a.row_stride = static_cast<int32_t>(row);
+  a.v_offset = static_cast<int64_t>(plan->page_size) * row;
+  a.page_stride = 2 * a.v_offset;
+  a.num_kv_heads = plan->num_kv_heads;
+  a.page_size = plan->page_size;
+  a.head_dim = plan->head_dim;
+  const hipError_t e = pka::launch_gather(a, plan->info.batch, stream);
+  if (e != hipSuccess) return hip_error("debug_gather launch", e);
+  return PKA_OK;
+}
+
+void pka_plan_destroy(pka_plan* plan) {
+  if (!plan_ok(plan)) return;
+  if (plan->staging) (void)hipHostFree(plan->staging);
+  plan->magic = 0;
+  delete plan;
+}
+
+}  // extern "C"

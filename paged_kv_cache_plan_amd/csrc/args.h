@@ -1,0 +1,73 @@
+// Kernel argument blocks shared by the host launchers and the kernels.
+#pragma once
+
+#include <cstdint>
+
+namespace pka {
+
+// Arguments of the attention kernels (prefill and decode).  Element offsets
+// count bf16 elements.
+struct AttnArgs {
+  const uint16_t* q;         // bf16 [total_q, Hq, D]
+  const uint16_t* k;         // paged: pool [num_pages, 2, ps, Hkv, D]; ragged: K [total_kv, Hkv, D]
+  const uint16_t* v;         // ragged: V [total_kv, Hkv, D]; paged: unused
+  void* o;                   // bf16 or fp32 [total_q, Hq, D]
+  float* lse;                // fp32 [total_q, Hq] or null
+  float* part_o;             // fp32 [num_partial_rows, D]
+  float* part_lse;           // fp32 [num_partial_rows]
+  const int32_t* units;      // [num_units][8]
+  const int32_t* req;        // [batch][8]
+  const int32_t* kv_indices; // [nnz] device copy
+  int64_t page_stride;       // elements per page: 2 * ps * Hkv * D
+  int64_t v_offset;          // elements from a K row to its V row: ps * Hkv * D (paged)
+  int32_t row_stride;        // elements between consecutive slots / tokens: Hkv * D
+  int32_t num_qo_heads;
+  int32_t group;             // Hq / Hkv
+  int32_t page_size;
+  int32_t page_shift;        // log2(page_size) when a power of two, else -1
+  int32_t out_fp32;
+  float scale_log2;          // sm_scale * log2(e): logits in base-2 units
+};
+
+// Arguments of the split-KV merge that follows an attention launch.
+struct MergeArgs {
+  const float* part_o;
+  const float* part_lse;
+  const int32_t* groups;     // [num_groups][8]
+  const int32_t* req;
+  void* o;
+  float* lse;
+  int32_t num_qo_heads;
+  int32_t group;
+  int32_t out_fp32;
+};
+
+// Arguments of the standalone merge of attention states.
+struct MergeStatesArgs {
+  const float* v;            // [n, S, H, D]
+  const float* s;            // [n, S, H]
+  void* v_out;               // [n, H, D]
+  float* s_out;              // [n, H] or null
+  int64_t n;
+  int32_t num_states;
+  int32_t num_heads;
+  int32_t head_dim;
+  int32_t out_fp32;
+};
+
+// Arguments of the test-only page gather.
+struct GatherArgs {
+  const uint16_t* pool;
+  uint16_t* k_out;
+  uint16_t* v_out;
+  const int32_t* req;
+  const int32_t* kv_indices;
+  int64_t page_stride;
+  int64_t v_offset;
+  int32_t row_stride;
+  int32_t num_kv_heads;
+  int32_t page_size;
+  int32_t head_dim;
+};
+
+}  // namespace pka

@@ -1,0 +1,254 @@
+// Single-token decode attention over a paged (or ragged dense) KV cache, gfx950.
+//
+// One workgroup = one work unit (request r, KV head hk, key range
+// [kv_lo, kv_hi)).  The G query heads that share KV head hk are processed
+// together so each K/V byte is read from HBM once.  The four waves take
+// interleaved 32-key steps of the range and keep independent online-softmax
+// states, merged through LDS at the end (the recursive-attention identity:
+// FlashInfer documentation, "Attention States and Recursive Attention").
+//
+// Per 32-key step of one wave:
+//   K        loaded from global straight into the A operand of
+//            v_mfma_f32_16x16x32_bf16 (lane: key l % 16, 8 consecutive d);
+//   S^T      = K . Q^T, query heads as MFMA columns (up to 16);
+//   softmax  fp32, base 2, row max over the four 16-lane rows with
+//            v_permlane16_swap / v_permlane32_swap;
+//   V        loaded 16 bytes per key, transposed in registers into a
+//            wave-private V^T tile in LDS, whose key order matches the order
+//            in which the S^T accumulator holds the scores, so P^T is the
+//            accumulator itself rounded to bf16;
+//   O^T     += V^T . P^T.
+// The kernel is bound by HBM bandwidth; the MFMA padding of G < 16 heads to
+// 16 columns costs matrix-core time that is otherwise idle.
+#include "args.h"
+#include "device.h"
+#include "launch.h"
+
+namespace pka {
+namespace {
+
+constexpr int kTK = 32;  // keys per wave step
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+
+// V^T row chunk swizzle (4 chunks of 8 keys per 32-key row).
+__device__ __forceinline__ int dvt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
+
+template <int D, bool PAGED>
+__global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+  constexpr int CPR = D / 8;   // 16-byte chunks per row
+  constexpr int DS = D / 32;   // k-steps of the S^T MFMA
+  constexpr int DB = D / 16;   // 16-row d blocks of O^T
+  constexpr int VT_ELEMS = D * kTK;               // per-wave V^T tile (bf16)
+  constexpr int MERGE_BYTES = kWaves * 16 * (D + 2) * 4;
+  constexpr int VT_BYTES = kWaves * VT_ELEMS * 2;
+  constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
+  __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int32_t* unit = a.units + static_cast<int64_t>(blockIdx.x) * 8;
+  const int r = unit[0], hk = unit[1];
+  const int kv_lo = unit[4], kv_hi = unit[5], prow = unit[6];
+  const int32_t* rq = a.req + static_cast<int64_t>(r) * 8;
+  const int qo_begin = rq[0], kv_base = rq[2];
+  const int G = a.group, Hq = a.num_qo_heads;
+
+  const int col = lane & 15;  // query head within the group (MFMA column)
+  const int g4 = lane >> 4;   // 16-lane row
+  const bool col_ok = col < G;
+
+  bf16x8 qreg[DS];
+  {
+    const uint16_t* qp = a.q + (static_cast<int64_t>(qo_begin) * Hq + hk * G + (col_ok ? col : 0)) * D + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(col_ok ? ld16(qp + 32 * s) : u32x4{0, 0, 0, 0});
+  }
+
+  const int ps = a.page_size, pshift = a.page_shift;
+  auto row_off = [&](int key) -> int64_t {  // element offset of the K row of `key`
+    if constexpr (PAGED) {
+      const int pg = pshift >= 0 ? (key >> pshift) : (key / ps);
+      const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
+      return static_cast<int64_t>(a.kv_indices[kv_base + pg]) * a.page_stride +
+             static_cast<int64_t>(slot) * a.row_stride;
+    } else {
+      return static_cast<int64_t>(kv_base + key) * a.row_stride;
+    }
+  };
+  const uint16_t* kb_ptr = a.k + hk * D;
+  const uint16_t* vb_ptr = PAGED ? kb_ptr + a.v_offset : a.v + hk * D;
+
+  // V loader: lane handles chunk vc of the 8 keys in slot group vg.
+  const int vc = lane % CPR, vg = lane / CPR;
+  const bool v_lane = vg < 4;
+  uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * VT_ELEMS;
+
+  f32x4 o[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) o[b] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kTK - 1) / kTK : 0;
+  for (int t = wave; t < n_tiles; t += kWaves) {
+    const int k0 = kv_lo + t * kTK;
+    // K operand: keys k0 + 16 kb + col, d = 32 s + 8 g4 .. + 8
+    u32x4 ka[2][DS];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = k0 + 16 * kb + col;
+      if (key < kv_hi) {
+        const uint16_t* p = kb_ptr + row_off(key) + 8 * g4;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) ka[kb][s] = ld16(p + 32 * s);
+      } else {
+#pragma unroll
+        for (int s = 0; s < DS; ++s) ka[kb][s] = u32x4{0, 0, 0, 0};
+      }
+    }
+    // V rows for slots 8 vg + j: key 4 vg + j (j < 4), 16 + 4 vg + j - 4 (j >= 4)
+    u32x4 vv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = k0 + (j < 4 ? 4 * vg + j : 16 + 4 * vg + (j - 4));
+      vv[j] = (v_lane && key < kv_hi) ? ld16(vb_ptr + row_off(key) + 8 * vc) : u32x4{0, 0, 0, 0};
+    }
+
+    f32x4 s[2];
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      s[kb] = f32x4{};
+#pragma unroll
+      for (int st = 0; st < DS; ++st)
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kb][st]), qreg[st], s[kb], 0, 0, 0);
+    }
+
+    // transpose V into the wave's V^T tile
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    if (v_lane) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int d = 8 * vc + e;
+        const int w = e >> 1;
+        u32x4 pk;
+#pragma unroll
+        for (int h = 0; h < 4; ++h)
+          pk[h] = (e & 1) ? pack_hi16(vv[2 * h][w], vv[2 * h + 1][w]) : pack_lo16(vv[2 * h][w], vv[2 * h + 1][w]);
+        st16(vt + d * kTK + ((vg ^ dvt_swz(d)) * 8), pk);
+      }
+    }
+    __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+
+    // mask keys past the range; S^T lane holds keys 16 kb + 4 g4 + i
+    if (k0 + kTK > kv_hi) {
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          if (k0 + 16 * kb + 4 * g4 + i >= kv_hi) s[kb][i] = -INFINITY;
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mx = fmaxf(mx, s[kb][i]);
+    mx = xor16_max(mx);
+    mx = xor32_max(mx);
+    const float m_new = fmaxf(m_run, mx * sl2);
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_use);
+    float rs = 0.f;
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float p = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -m_use));
+        s[kb][i] = p;
+        rs += p;
+      }
+    l_run = l_run * alpha + rs;
+    m_run = m_new;
+#pragma unroll
+    for (int b = 0; b < DB; ++b) o[b] *= alpha;
+
+    u32x4 pw;
+    pw[0] = pack_bf16(s[0][0], s[0][1]);
+    pw[1] = pack_bf16(s[0][2], s[0][3]);
+    pw[2] = pack_bf16(s[1][0], s[1][1]);
+    pw[3] = pack_bf16(s[1][2], s[1][3]);
+    const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+    for (int b = 0; b < DB; ++b) {
+      const int d = 16 * b + col;
+      const bf16x8 va = as_bf16x8(ld16(vt + d * kTK + ((g4 ^ dvt_swz(d)) * 8)));
+      o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[b], 0, 0, 0);
+    }
+  }
+
+  // ---- merge the four waves' states -------------------------------------
+  float l_tot = xor32_sum(xor16_sum(l_run));
+  __syncthreads();  // every wave is done with its V^T tile
+  float* wo = reinterpret_cast<float*>(smem);            // [wave][16][D]
+  float* wm = wo + kWaves * 16 * D;                       // [wave][16]
+  float* wl = wm + kWaves * 16;                           // [wave][16]
+  if (g4 == 0) {
+    wm[wave * 16 + col] = m_run;
+    wl[wave * 16 + col] = l_tot;
+  }
+#pragma unroll
+  for (int b = 0; b < DB; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) wo[(wave * 16 + col) * D + 16 * b + 4 * g4 + i] = o[b][i];
+  __syncthreads();
+
+  for (int idx = tid; idx < G * D; idx += kThreads) {
+    const int c = idx / D, d = idx - c * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, wm[w * 16 + c]);
+    float L = 0.f, acc = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) {
+        const float sc = fast_exp2(wm[w * 16 + c] - M);
+        L += sc * wl[w * 16 + c];
+        acc += sc * wo[(w * 16 + c) * D + d];
+      }
+    }
+    const bool seen = L > 0.f;
+    const float val = seen ? acc / L : 0.f;
+    const float lse = seen ? M + __log2f(L) : -INFINITY;
+    if (prow < 0) {
+      const int64_t orow = static_cast<int64_t>(qo_begin) * Hq + hk * G + c;
+      if (a.out_fp32)
+        static_cast<float*>(a.o)[orow * D + d] = val;
+      else
+        static_cast<__bf16*>(a.o)[orow * D + d] = static_cast<__bf16>(val);
+      if (a.lse && d == 0) a.lse[orow] = lse;
+    } else {
+      a.part_o[static_cast<int64_t>(prow + c) * D + d] = val;
+      if (d == 0) a.part_lse[prow + c] = lse;
+    }
+  }
+}
+
+template <int D>
+hipError_t launch_decode_d(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
+  if (paged)
+    decode_kernel<D, true><<<grid, kThreads, 0, stream>>>(a);
+  else
+    decode_kernel<D, false><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_decode(const AttnArgs& a, int head_dim, bool paged, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  return head_dim == 128 ? launch_decode_d<128>(a, paged, grid, stream)
+                         : launch_decode_d<64>(a, paged, grid, stream);
+}
+
+}  // namespace pka

@@ -1,0 +1,145 @@
+// Merging attention states (FlashInfer documentation, "Attention States and
+// Recursive Attention" and "flashinfer.cascade - Merge Attention States"; the
+// base-2 LSE of flashinfer-trace discussion #15, "Notes on fa3_gqa_prefill_v1").
+//
+// For states (o_s, lse_s): M = max lse_s, w_s = 2^(lse_s - M),
+//   lse = M + log2 sum w_s,   o = sum w_s o_s / sum w_s,
+// empty states (lse = -inf) weigh 0, all-empty rows give (0, -inf).  States
+// are combined in index order, so results are run-to-run deterministic.
+//
+// Both kernels are memory-bound: each thread owns 4 consecutive d of one row
+// and reads every state's 16 bytes once.  Also here: the test-only page
+// gather, which copies exactly the K/V rows the attention kernels address.
+#include "args.h"
+#include "device.h"
+#include "launch.h"
+
+namespace pka {
+namespace {
+
+constexpr int kThreads = 256;
+
+__device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v, bool fp32) {
+  if (fp32) {
+    *reinterpret_cast<f32x4*>(static_cast<float*>(out) + idx) = v;
+  } else {
+    u32x2 pk;
+    pk[0] = pack_bf16(v[0], v[1]);
+    pk[1] = pack_bf16(v[2], v[3]);
+    *reinterpret_cast<u32x2*>(static_cast<uint16_t*>(out) + idx) = pk;
+  }
+}
+
+// One workgroup per split group: rows [row0, row1) of (request, kv head).
+template <int D>
+__global__ __launch_bounds__(kThreads) void merge_split_kernel(MergeArgs a) {
+  constexpr int C4 = D / 4;
+  const int32_t* g = a.groups + static_cast<int64_t>(blockIdx.x) * 8;
+  const int r = g[0], hk = g[1], row0 = g[2], row1 = g[3], pbase = g[4], S = g[5];
+  const int nrows = row1 - row0;
+  const int qo_begin = a.req[static_cast<int64_t>(r) * 8];
+  const int G = a.group, Hq = a.num_qo_heads;
+  for (int it = threadIdx.x; it < nrows * C4; it += kThreads) {
+    const int row = it / C4, c4 = it - row * C4;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_lse[pbase + s * nrows + row]);
+    float W = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const int64_t prow = pbase + s * nrows + row;
+        const float w = fast_exp2(a.part_lse[prow] - M);
+        if (w > 0.f) {
+          W += w;
+          acc += w * *reinterpret_cast<const f32x4*>(a.part_o + prow * D + 4 * c4);
+        }
+      }
+    }
+    const bool seen = W > 0.f;
+    const float inv = seen ? 1.f / W : 0.f;
+    const int p = row0 + row;
+    const int tok = p / G;
+    const int64_t orow = static_cast<int64_t>(qo_begin + tok) * Hq + hk * G + (p - tok * G);
+    store4(a.o, orow * D + 4 * c4, acc * inv, a.out_fp32 != 0);
+    if (a.lse && c4 == 0) a.lse[orow] = seen ? M + __log2f(W) : -INFINITY;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void merge_states_kernel(MergeStatesArgs a) {
+  const int D = a.head_dim, C4 = D / 4, H = a.num_heads, S = a.num_states;
+  const int64_t items = a.n * H * C4;
+  for (int64_t it = static_cast<int64_t>(blockIdx.x) * kThreads + threadIdx.x; it < items;
+       it += static_cast<int64_t>(gridDim.x) * kThreads) {
+    const int c4 = static_cast<int>(it % C4);
+    const int64_t nh = it / C4;
+    const int h = static_cast<int>(nh % H);
+    const int64_t i = nh / H;
+    const float* sp = a.s + i * S * H + h;
+    float M = -INFINITY;
+    for (int s = 0; s < S; ++s) M = fmaxf(M, sp[static_cast<int64_t>(s) * H]);
+    float W = 0.f;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    if (M != -INFINITY) {
+      for (int s = 0; s < S; ++s) {
+        const float w = fast_exp2(sp[static_cast<int64_t>(s) * H] - M);
+        if (w > 0.f) {
+          W += w;
+          acc += w * *reinterpret_cast<const f32x4*>(a.v + ((i * S + s) * H + h) * D + 4 * c4);
+        }
+      }
+    }
+    const bool seen = W > 0.f;
+    store4(a.v_out, (i * H + h) * D + 4 * c4, acc * (seen ? 1.f / W : 0.f), a.out_fp32 != 0);
+    if (a.s_out && c4 == 0) a.s_out[i * H + h] = seen ? M + __log2f(W) : -INFINITY;
+  }
+}
+
+// One workgroup per request: copy its kv_len K and V rows (all KV heads) into
+// the dense outputs, addressing them exactly like the attention kernels do.
+__global__ __launch_bounds__(kThreads) void gather_kernel(GatherArgs a) {
+  const int32_t* rq = a.req + static_cast<int64_t>(blockIdx.x) * 8;
+  const int kv_base = rq[2], kv_len = rq[3], dense = rq[4];
+  const int CPR = a.head_dim / 8;
+  const int per_tok = a.num_kv_heads * CPR;
+  const int64_t items = static_cast<int64_t>(kv_len) * per_tok;
+  for (int64_t it = threadIdx.x; it < items; it += kThreads) {
+    const int t = static_cast<int>(it / per_tok);
+    const int rem = static_cast<int>(it - static_cast<int64_t>(t) * per_tok);
+    const int hk = rem / CPR, c = rem - hk * CPR;
+    const int pg = a.kv_indices[kv_base + t / a.page_size];
+    const int slot = t % a.page_size;
+    const int64_t src = static_cast<int64_t>(pg) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride +
+                        hk * a.head_dim + 8 * c;
+    const int64_t dst = (static_cast<int64_t>(dense + t) * a.num_kv_heads + hk) * a.head_dim + 8 * c;
+    st16(a.k_out + dst, ld16(a.pool + src));
+    st16(a.v_out + dst, ld16(a.pool + src + a.v_offset));
+  }
+}
+
+}  // namespace
+
+hipError_t launch_merge(const MergeArgs& a, int head_dim, int grid, hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128)
+    merge_split_kernel<128><<<grid, kThreads, 0, stream>>>(a);
+  else
+    merge_split_kernel<64><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream) {
+  const int64_t items = a.n * a.num_heads * (a.head_dim / 4);
+  if (items <= 0) return hipSuccess;
+  int64_t grid = (items + kThreads - 1) / kThreads;
+  if (grid > 65536) grid = 65536;
+  merge_states_kernel<<<static_cast<int>(grid), kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather(const GatherArgs& a, int batch, hipStream_t stream) {
+  if (batch <= 0) return hipSuccess;
+  gather_kernel<<<batch, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace pka

@@ -1,0 +1,260 @@
+// Host planner: validation, kv_len, tiling, split-KV and ordering of work units.
+#include "planner.h"
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+
+namespace pka {
+namespace {
+
+int fail(std::string* err, int code, const char* fmt, long long a = 0, long long b = 0,
+         long long c = 0) {
+  char buf[512];
+  std::snprintf(buf, sizeof(buf), fmt, a, b, c);
+  if (err) *err = buf;
+  return code;
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int32_t align_words(int64_t w) { return static_cast<int32_t>(ceil_div(w, 64) * 64); }
+
+struct Unit {
+  int32_t f[kUnitWords];
+  int64_t cost;  // keys processed, the ordering key
+  int32_t seq;   // creation order, the tie-break that keeps ordering deterministic
+};
+
+}  // namespace
+
+int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
+  const bool ragged = (in.flags & kFlagRagged) != 0;
+  const int B = in.batch;
+  if (B < 0) return fail(err, kInvalid, "batch must be >= 0 (got %lld)", B);
+  if (!in.qo_indptr || !in.kv_indptr) return fail(err, kInvalid, "qo_indptr and kv_indptr must not be NULL");
+  if (!ragged && B > 0 && !in.kv_last_page_len)
+    return fail(err, kInvalid, "kv_last_page_len must not be NULL for a paged KV cache");
+  if (in.num_qo_heads <= 0 || in.num_kv_heads <= 0)
+    return fail(err, kInvalid, "head counts must be positive (Hq=%lld, Hkv=%lld)", in.num_qo_heads,
+                in.num_kv_heads);
+  if (in.num_qo_heads % in.num_kv_heads != 0)
+    return fail(err, kUnsupported, "num_qo_heads (%lld) must be a multiple of num_kv_heads (%lld)",
+                in.num_qo_heads, in.num_kv_heads);
+  if (in.head_dim != 64 && in.head_dim != 128)
+    return fail(err, kUnsupported, "head_dim %lld is not supported (64 or 128)", in.head_dim);
+  const int ps = ragged ? 1 : in.page_size;
+  if (!ragged && (ps < 1 || ps > 128))
+    return fail(err, kUnsupported, "page_size %lld is outside [1, 128]", ps);
+  const int G = in.num_qo_heads / in.num_kv_heads;
+  const int Hkv = in.num_kv_heads;
+
+  if (in.qo_indptr[0] != 0) return fail(err, kInvalid, "qo_indptr[0] must be 0 (got %lld)", in.qo_indptr[0]);
+  if (in.kv_indptr[0] != 0) return fail(err, kInvalid, "kv_indptr[0] must be 0 (got %lld)", in.kv_indptr[0]);
+  for (int r = 0; r < B; ++r) {
+    if (in.qo_indptr[r + 1] < in.qo_indptr[r])
+      return fail(err, kInvalid, "qo_indptr decreases at %lld (%lld -> %lld)", r, in.qo_indptr[r],
+                  in.qo_indptr[r + 1]);
+    if (in.kv_indptr[r + 1] < in.kv_indptr[r])
+      return fail(err, kInvalid, "kv_indptr decreases at %lld (%lld -> %lld)", r, in.kv_indptr[r],
+                  in.kv_indptr[r + 1]);
+  }
+  const int32_t nnz = in.kv_indptr[B];
+  if (!ragged) {
+    if (in.nnz_pages != nnz)
+      return fail(err, kInvalid, "kv_indptr[batch] = %lld but nnz_pages = %lld", nnz, in.nnz_pages);
+    if (in.check_indices) {
+      if (nnz > 0 && !in.kv_indices) return fail(err, kInvalid, "kv_indices must not be NULL");
+      if (in.num_pages <= 0 && nnz > 0)
+        return fail(err, kInvalid, "num_pages_in_pool must be positive (got %lld)", in.num_pages);
+      for (int32_t i = 0; i < nnz; ++i) {
+        const int32_t p = in.kv_indices[i];
+        if (p < 0 || p >= in.num_pages)
+          return fail(err, kInvalid, "kv_indices[%lld] = %lld is outside [0, %lld)", i, p, in.num_pages);
+      }
+    }
+  }
+
+  // kv_len per request: every page but the last is full.
+  std::vector<int64_t> kv_len(B), qo_len(B);
+  int64_t total_kv = 0;
+  int32_t max_qo = 0;
+  for (int r = 0; r < B; ++r) {
+    qo_len[r] = in.qo_indptr[r + 1] - in.qo_indptr[r];
+    max_qo = std::max<int32_t>(max_qo, static_cast<int32_t>(qo_len[r]));
+    const int64_t span = in.kv_indptr[r + 1] - in.kv_indptr[r];
+    if (ragged) {
+      kv_len[r] = span;
+    } else {
+      const int32_t last = in.kv_last_page_len[r];
+      if (span == 0) {
+        if (last != 0)
+          return fail(err, kInvalid, "request %lld has no pages but kv_last_page_len = %lld", r, last);
+        kv_len[r] = 0;
+      } else {
+        if (last < 1 || last > ps)
+          return fail(err, kInvalid, "kv_last_page_len[%lld] = %lld is outside [1, page_size=%lld]", r,
+                      last, ps);
+        kv_len[r] = (span - 1) * ps + last;
+      }
+    }
+    if (kv_len[r] > (int64_t(1) << 30)) return fail(err, kUnsupported, "request %lld: kv_len too large", r);
+    if (qo_len[r] * G > (int64_t(1) << 30)) return fail(err, kUnsupported, "request %lld: qo_len too large", r);
+    total_kv += kv_len[r];
+  }
+
+  const bool no_split = (in.flags & kFlagDisableSplit) != 0;
+  const bool decode = B > 0 && max_qo <= 1 && G <= kDecodeMaxGroup;
+
+  std::vector<Unit> units;
+  // one entry per (request, kv head, row block): the KV range before splitting
+  struct Block { int32_t r, hk, row0, row1; int64_t kv_hi; };
+  std::vector<Block> blocks;
+  int32_t block_rows;
+  if (decode) {
+    block_rows = G;
+    for (int r = 0; r < B; ++r) {
+      if (qo_len[r] == 0) continue;
+      for (int hk = 0; hk < Hkv; ++hk) blocks.push_back({r, hk, 0, G, kv_len[r]});
+    }
+  } else {
+    block_rows = kPrefillBlockRows;
+    for (int r = 0; r < B; ++r) {
+      if (qo_len[r] == 0) continue;
+      const int64_t rows = qo_len[r] * G;
+      for (int hk = 0; hk < Hkv; ++hk) {
+        for (int64_t r0 = 0; r0 < rows; r0 += block_rows) {
+          const int64_t r1 = std::min<int64_t>(rows, r0 + block_rows);
+          int64_t hi = kv_len[r];
+          if (in.causal) {
+            const int64_t last_tok = (r1 - 1) / G;  // bottom-right: sees j <= i + kv_len - qo_len
+            hi = std::min<int64_t>(hi, last_tok + kv_len[r] - qo_len[r] + 1);
+            hi = std::max<int64_t>(hi, 0);
+          }
+          blocks.push_back({r, hk, static_cast<int32_t>(r0), static_cast<int32_t>(r1), hi});
+        }
+      }
+    }
+  }
+
+  // Split-KV policy.  Decode: cut long KV into chunks so that the launch has
+  // several units per compute unit.  Prefill: only when the batch has too few
+  // row blocks to fill the chip.
+  int64_t chunk = 0;
+  if (!no_split && !blocks.empty()) {
+    if (decode) {
+      int64_t keys = 0;
+      for (const Block& b : blocks) keys += b.kv_hi;
+      chunk = ceil_div(keys, int64_t(in.num_cus) * 8);
+      chunk = std::min<int64_t>(2048, std::max<int64_t>(256, ceil_div(chunk, 128) * 128));
+    } else if (static_cast<int64_t>(blocks.size()) < 2 * in.num_cus) {
+      int64_t tiles = 0;
+      for (const Block& b : blocks) tiles += ceil_div(b.kv_hi, kPrefillBlockKeys);
+      const int64_t chunk_tiles = std::max<int64_t>(8, ceil_div(tiles, 4 * int64_t(in.num_cus)));
+      chunk = chunk_tiles * kPrefillBlockKeys;
+    }
+    if (in.kv_chunk_override > 0) {
+      const int64_t q = decode ? kDecodeTileKeys : kPrefillBlockKeys;
+      chunk = std::max<int64_t>(q, ceil_div(in.kv_chunk_override, q) * q);
+    }
+  }
+
+  std::vector<int32_t> merge;
+  int64_t partial_rows = 0;
+  bool any_split = false;
+  for (const Block& b : blocks) {
+    const int64_t n_split = (chunk > 0 && b.kv_hi > chunk) ? ceil_div(b.kv_hi, chunk) : 1;
+    const int32_t nrows = b.row1 - b.row0;
+    int64_t pbase = -1;
+    if (n_split > 1) {
+      any_split = true;
+      pbase = partial_rows;
+      partial_rows += n_split * nrows;
+      if (partial_rows > (int64_t(1) << 30)) return fail(err, kUnsupported, "too many partial rows");
+      merge.insert(merge.end(), {b.r, b.hk, b.row0, b.row1, static_cast<int32_t>(pbase),
+                                 static_cast<int32_t>(n_split), 0, 0});
+    }
+    for (int64_t s = 0; s < n_split; ++s) {
+      Unit u{};
+      const int64_t lo = n_split > 1 ? s * chunk : 0;
+      const int64_t hi = n_split > 1 ? std::min<int64_t>(b.kv_hi, lo + chunk) : b.kv_hi;
+      u.f[kUnitRequest] = b.r;
+      u.f[kUnitKvHead] = b.hk;
+      u.f[kUnitRowBegin] = b.row0;
+      u.f[kUnitRowEnd] = b.row1;
+      u.f[kUnitKvBegin] = static_cast<int32_t>(lo);
+      u.f[kUnitKvEnd] = static_cast<int32_t>(hi);
+      u.f[kUnitPartialRow] = n_split > 1 ? static_cast<int32_t>(pbase + s * nrows) : -1;
+      u.f[kUnitReserved] = 0;
+      u.cost = (hi - lo) * nrows + 1;
+      u.seq = static_cast<int32_t>(units.size());
+      units.push_back(u);
+    }
+  }
+  if (units.size() > size_t(1) << 30) return fail(err, kUnsupported, "too many work units");
+
+  // Longest-first order: the hardware hands out workgroups roughly in index
+  // order, so big units start first and small ones fill the tail.
+  std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b) {
+    if (a.cost != b.cost) return a.cost > b.cost;
+    return a.seq < b.seq;
+  });
+
+  // Assemble the image.
+  const int32_t n_units = static_cast<int32_t>(units.size());
+  const int32_t n_merge = static_cast<int32_t>(merge.size() / kMergeWords);
+  const int32_t off_units = align_words(kHdrWords);
+  const int32_t off_req = off_units + align_words(int64_t(n_units) * kUnitWords);
+  const int32_t off_merge = off_req + align_words(int64_t(B) * kReqWords);
+  const int32_t off_idx = off_merge + align_words(int64_t(n_merge) * kMergeWords);
+  const int64_t n_idx = ragged ? 0 : nnz;
+  const int64_t total_words = off_idx + align_words(std::max<int64_t>(n_idx, 1));
+  out->image.assign(static_cast<size_t>(total_words), 0);
+  int32_t* im = out->image.data();
+  im[kHdrMagic] = kMagic;
+  im[kHdrKernel] = decode ? kDecode : kPrefill;
+  im[kHdrNumUnits] = n_units;
+  im[kHdrNumMerge] = n_merge;
+  im[kHdrBatch] = B;
+  im[kHdrNnz] = ragged ? 0 : nnz;
+  im[kHdrOffUnits] = off_units;
+  im[kHdrOffReq] = off_req;
+  im[kHdrOffMerge] = off_merge;
+  im[kHdrOffIndices] = off_idx;
+  im[kHdrNumPartialRows] = static_cast<int32_t>(partial_rows);
+  im[kHdrBlockRows] = block_rows;
+  im[kHdrKvChunk] = any_split ? static_cast<int32_t>(chunk) : 0;
+  im[kHdrFlags] = static_cast<int32_t>(in.flags);
+  for (int32_t i = 0; i < n_units; ++i)
+    std::memcpy(im + off_units + int64_t(i) * kUnitWords, units[i].f, sizeof(units[i].f));
+  int64_t dense = 0;
+  for (int r = 0; r < B; ++r) {
+    int32_t* q = im + off_req + int64_t(r) * kReqWords;
+    q[kReqQoBegin] = in.qo_indptr[r];
+    q[kReqQoLen] = static_cast<int32_t>(qo_len[r]);
+    q[kReqKvBegin] = in.kv_indptr[r];
+    q[kReqKvLen] = static_cast<int32_t>(kv_len[r]);
+    q[kReqKvDense] = static_cast<int32_t>(dense);
+    dense += kv_len[r];
+  }
+  if (dense > (int64_t(1) << 31) - 1) return fail(err, kUnsupported, "total kv length too large");
+  if (n_merge) std::memcpy(im + off_merge, merge.data(), merge.size() * sizeof(int32_t));
+  if (n_idx && in.kv_indices) std::memcpy(im + off_idx, in.kv_indices, size_t(n_idx) * sizeof(int32_t));
+
+  out->kernel = decode ? kDecode : kPrefill;
+  out->num_units = n_units;
+  out->num_merge = n_merge;
+  out->num_partial_rows = static_cast<int32_t>(partial_rows);
+  out->block_rows = block_rows;
+  out->kv_chunk = any_split ? static_cast<int32_t>(chunk) : 0;
+  out->total_q = in.qo_indptr[B];
+  out->total_kv = total_kv;
+  const size_t o_bytes = static_cast<size_t>(partial_rows) * in.head_dim * sizeof(float);
+  out->partial_lse_offset = (o_bytes + 255) / 256 * 256;
+  out->float_ws_bytes = out->partial_lse_offset +
+                        (static_cast<size_t>(partial_rows) * sizeof(float) + 255) / 256 * 256;
+  if (out->float_ws_bytes == 0) out->float_ws_bytes = 256;
+  return kOk;
+}
+
+}  // namespace pka

@@ -1,0 +1,128 @@
+// Host planner for batch attention over a paged KV cache.  Plain C++17 with
+// no HIP dependency, so it builds and runs on a machine without a GPU.
+//
+// It turns the flat page table (flashinfer-trace discussion #15, "Notes on
+// fa3_gqa_prefill_v1": kv_indptr / kv_indices / kv_last_page_len) and the
+// ragged query layout into fixed-size integer work arrays that the kernels
+// read.  Planning from host arrays, with the result shipped to the device by
+// one asynchronous copy, follows the FlashInfer 0.2 release blog ("faster plan
+// function").  Whether to split one request's KV over several work units is a
+// plan-time choice that a flag can switch off (flashinfer-trace discussion
+// #15, table of tunable runtime knobs: disable_split_kv).
+#pragma once
+
+#include <cstddef>
+#include <cstdint>
+#include <string>
+#include <vector>
+
+namespace pka {
+
+// Layout of the int workspace image (int32 words).  Every section starts on a
+// 64-word (256-byte) boundary.
+enum HeaderField : int {
+  kHdrMagic = 0,
+  kHdrKernel,
+  kHdrNumUnits,
+  kHdrNumMerge,
+  kHdrBatch,
+  kHdrNnz,
+  kHdrOffUnits,
+  kHdrOffReq,
+  kHdrOffMerge,
+  kHdrOffIndices,
+  kHdrNumPartialRows,
+  kHdrBlockRows,
+  kHdrKvChunk,
+  kHdrFlags,
+  kHdrWords = 16
+};
+constexpr int32_t kMagic = 0x31414b50;  // "PKA1"
+
+// One work unit = one workgroup of the attention launch.
+enum UnitField : int {
+  kUnitRequest = 0,
+  kUnitKvHead,
+  kUnitRowBegin,  // packed row = token * group + head-in-group, within the request
+  kUnitRowEnd,
+  kUnitKvBegin,   // first key (token index within the request)
+  kUnitKvEnd,     // one past the last key
+  kUnitPartialRow,  // -1: write o/lse; otherwise first fp32 partial row
+  kUnitReserved,
+  kUnitWords = 8
+};
+
+// Per-request facts the kernels need.
+enum ReqField : int {
+  kReqQoBegin = 0,
+  kReqQoLen,
+  kReqKvBegin,   // paged: offset into kv_indices; ragged: first token row of k/v
+  kReqKvLen,
+  kReqKvDense,   // first row of this request in a dense [total_kv, ...] copy
+  kReqWords = 8
+};
+
+// A split group: one (request, kv head, row block) whose KV was cut into
+// num_splits chunks; chunk s wrote partial rows
+// partial_row_begin + s * (row_end - row_begin) + (row - row_begin).
+enum MergeField : int {
+  kMergeRequest = 0,
+  kMergeKvHead,
+  kMergeRowBegin,
+  kMergeRowEnd,
+  kMergePartialBegin,
+  kMergeNumSplits,
+  kMergeWords = 8
+};
+
+enum Kernel : int { kPrefill = 0, kDecode = 1 };
+
+// Tile shapes the kernels are built for.
+constexpr int kPrefillBlockRows = 128;  // packed query rows per prefill workgroup
+constexpr int kPrefillBlockKeys = 64;   // keys per prefill KV tile
+constexpr int kDecodeTileKeys = 32;     // keys per decode wave step
+constexpr int kDecodeMaxGroup = 16;     // decode kernel holds up to 16 query heads per KV head
+
+constexpr uint32_t kFlagDisableSplit = 0x1u;
+constexpr uint32_t kFlagOutFp32 = 0x2u;
+constexpr uint32_t kFlagRagged = 0x4u;
+
+enum Status : int { kOk = 0, kInvalid = 1, kUnsupported = 2, kWorkspace = 3, kHip = 4 };
+
+struct PlanInput {
+  const int32_t* qo_indptr = nullptr;
+  const int32_t* kv_indptr = nullptr;
+  const int32_t* kv_indices = nullptr;  // may be null when only sizes are wanted
+  const int32_t* kv_last_page_len = nullptr;
+  int32_t batch = 0;
+  int32_t nnz_pages = 0;
+  int32_t num_pages = 0;
+  int32_t num_qo_heads = 0;
+  int32_t num_kv_heads = 0;
+  int32_t head_dim = 0;
+  int32_t page_size = 0;
+  int32_t causal = 0;
+  uint32_t flags = 0;
+  bool check_indices = true;   // validate kv_indices (needs the array)
+  int32_t kv_chunk_override = 0;  // >0: keys per split chunk (tuning); 0: heuristic
+  int32_t num_cus = 256;          // compute units the split heuristic aims to fill
+};
+
+struct PlanResult {
+  int32_t kernel = kPrefill;
+  int32_t num_units = 0;
+  int32_t num_merge = 0;
+  int32_t num_partial_rows = 0;
+  int32_t block_rows = 0;
+  int32_t kv_chunk = 0;
+  int64_t total_q = 0;
+  int64_t total_kv = 0;
+  std::vector<int32_t> image;  // the int workspace image
+  size_t float_ws_bytes = 0;
+  size_t partial_lse_offset = 0;  // byte offset of partial lse inside the float workspace
+};
+
+// Validate and plan.  Returns a Status and fills *err on failure.
+int build_plan(const PlanInput& in, PlanResult* out, std::string* err);
+
+}  // namespace pka

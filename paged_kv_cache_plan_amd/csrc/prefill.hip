@@ -1,0 +1,315 @@
+// Prefill / append attention over a paged (or ragged dense) KV cache, gfx950.
+//
+// One workgroup = one work unit (request r, KV head hk, block of 128 packed
+// query rows, key range [kv_lo, kv_hi)).  Packed row p of a request is token
+// p / G and query head hk * G + p % G, so the G query heads that share a KV
+// head share every K/V tile the workgroup loads.
+//
+// PageAttention is block-sparse attention with page_size-wide blocks
+// (FlashInfer 0.2 release blog, "flexible block sparsity and vector
+// sparsity"), and the paged form differs from dense attention only in where
+// the K/V rows are read from (same blog, "FlashAttention-3 template with
+// block/vector sparsity": the gather sits in the producer's memory load).  The
+// same holds here: the page-table lookup happens in the tile loader; the
+// contraction and softmax code is shared by the paged and ragged variants.
+//
+// Per 64-key tile:
+//   loader   each thread fetches KPT keys x one 16-byte chunk of K and V,
+//            issued one tile ahead (page ids two tiles ahead); K goes to LDS
+//            row-major with an XOR swizzle, V is transposed in registers and
+//            stored as V^T so that the P.V operand is one 16-byte LDS read.
+//   S^T      = K . Q^T with v_mfma_f32_32x32x16_bf16: each wave owns 32 query
+//            rows as MFMA columns, so a lane holds 16 of a row's 32 scores per
+//            32-key block and the other 16 sit in lane l ^ 32.
+//   softmax  online, fp32, base 2 (sm_scale * log2 e folded into one FMA);
+//            row max needs one v_permlane32_swap; row sums stay per lane
+//            until the end.
+//   O^T     += V^T . P^T with the same MFMA; P^T is the S^T accumulator
+//            rounded to bf16 in place (no data movement), V^T comes from LDS.
+#include "args.h"
+#include "device.h"
+#include "launch.h"
+
+namespace pka {
+namespace {
+
+constexpr int kBM = 128;  // packed query rows per workgroup (4 waves x 32)
+constexpr int kBN = 64;   // keys per tile
+constexpr int kThreads = 256;
+
+// Position of key k (0..63) of a tile inside a V^T row.  Within each group of
+// 16 keys the order is 0-3, 8-11, 4-7, 12-15: exactly the key order in which
+// a lane of the S^T accumulator holds its scores, so P^T needs no shuffle.
+__device__ __forceinline__ int vt_pos(int k) {
+  return (k & ~15) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
+}
+// 16-byte chunk swizzles (XOR), chosen so that the MFMA operand reads are
+// bank-conflict free: K rows by key, V^T rows by d.
+__device__ __forceinline__ int k_swz(int key) { return key & 7; }
+__device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
+
+template <int D, bool PAGED, bool CAUSAL>
+__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
+  constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
+  constexpr int KPT = kBN * CPR / kThreads;  // keys per loader thread: 4 (D=128), 2 (D=64)
+  constexpr int DS = D / 16;                 // k-steps of the S^T MFMA
+  constexpr int DB = D / 32;                 // 32-row d blocks of O^T
+  static_assert(KPT == 2 || KPT == 4, "tile shape");
+
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * D];
+  __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kBN];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int32_t* unit = a.units + static_cast<int64_t>(blockIdx.x) * 8;
+  const int r = unit[0], hk = unit[1], row_begin = unit[2], row_end = unit[3];
+  const int kv_lo = unit[4], kv_hi = unit[5], prow = unit[6];
+  const int32_t* rq = a.req + static_cast<int64_t>(r) * 8;
+  const int qo_begin = rq[0], qo_len = rq[1], kv_base = rq[2], kv_len = rq[3];
+  const int G = a.group, Hq = a.num_qo_heads;
+
+  // ---- this lane's query row (MFMA column) --------------------------------
+  const int qcol = lane & 31, half = lane >> 5;
+  const int wrow0 = row_begin + wave * 32;
+  const bool wave_active = wrow0 < row_end;
+  const int my_row = wrow0 + qcol;
+  const bool row_ok = my_row < row_end;
+  const int tok = (row_ok ? my_row : wrow0) / G;
+  const int head = hk * G + ((row_ok ? my_row : wrow0) - tok * G);
+  const int lim = tok + kv_len - qo_len;  // last visible key (causal)
+  const int wave_lim = wrow0 / G + kv_len - qo_len;  // smallest limit in the wave
+
+  bf16x8 qreg[DS];
+  {
+    const uint16_t* qp = a.q + (static_cast<int64_t>(qo_begin + tok) * Hq + head) * D + 8 * half;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(row_ok ? ld16(qp + 16 * s) : u32x4{0, 0, 0, 0});
+  }
+
+  // ---- loader mapping -------------------------------------------------------
+  const int lc = tid % CPR;        // 16-byte chunk of the row
+  const int lj = tid / CPR;        // key group: keys KPT*lj .. KPT*lj + KPT-1
+  const int ps = a.page_size, pshift = a.page_shift;
+  const uint16_t* kbase = a.k + hk * D + 8 * lc;
+  const uint16_t* vbase = PAGED ? kbase + a.v_offset : a.v + hk * D + 8 * lc;
+
+  u32x4 kreg[KPT], vreg[KPT];
+  int ids_a[KPT], ids_b[KPT];
+
+  auto fetch_ids = [&](int k0, int* ids) {
+    if constexpr (PAGED) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int key = k0 + KPT * lj + i;
+        const int pg = pshift >= 0 ? (key >> pshift) : (key / ps);
+        ids[i] = key < kv_hi ? a.kv_indices[kv_base + pg] : 0;
+      }
+    }
+  };
+  auto fetch_data = [&](int k0, const int* ids) {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int key = k0 + KPT * lj + i;
+      if (key < kv_hi) {
+        int64_t off;
+        if constexpr (PAGED) {
+          const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
+          off = static_cast<int64_t>(ids[i]) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride;
+        } else {
+          off = static_cast<int64_t>(kv_base + key) * a.row_stride;
+        }
+        kreg[i] = ld16(kbase + off);
+        vreg[i] = ld16(vbase + off);
+      } else {
+        kreg[i] = u32x4{0, 0, 0, 0};
+        vreg[i] = u32x4{0, 0, 0, 0};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int key = KPT * lj + i;
+      st16(Ks + key * D + ((lc ^ k_swz(key)) * 8), kreg[i]);
+    }
+    const int p0 = vt_pos(KPT * lj);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * lc + e;
+      uint16_t* dst = Vt + d * kBN + (((p0 >> 3) ^ vt_swz(d)) * 8) + (p0 & 7);
+      const int w = e >> 1;
+      if constexpr (KPT == 4) {
+        u32x2 pk;
+        pk[0] = (e & 1) ? pack_hi16(vreg[0][w], vreg[1][w]) : pack_lo16(vreg[0][w], vreg[1][w]);
+        pk[1] = (e & 1) ? pack_hi16(vreg[2][w], vreg[3][w]) : pack_lo16(vreg[2][w], vreg[3][w]);
+        *reinterpret_cast<u32x2*>(dst) = pk;
+      } else {
+        *reinterpret_cast<uint32_t*>(dst) =
+            (e & 1) ? pack_hi16(vreg[0][w], vreg[1][w]) : pack_lo16(vreg[0][w], vreg[1][w]);
+      }
+    }
+  };
+
+  // ---- running state ---------------------------------------------------------
+  f32x16 o[DB];
+#pragma unroll
+  for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+  const float sl2 = a.scale_log2;
+
+  const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kBN - 1) / kBN : 0;
+  if (n_tiles > 0) {
+    fetch_ids(kv_lo, ids_a);
+    fetch_data(kv_lo, ids_a);
+    if (n_tiles > 1) fetch_ids(kv_lo + kBN, ids_b);
+  }
+
+  for (int t = 0; t < n_tiles; ++t) {
+    const int k0 = kv_lo + t * kBN;
+    store_tile();
+    __syncthreads();
+    if (t + 1 < n_tiles) {
+      fetch_data(k0 + kBN, ids_b);
+      if (t + 2 < n_tiles) fetch_ids(k0 + 2 * kBN, ids_b);
+    }
+
+    if (wave_active) {
+      // S^T = K . Q^T for two 32-key blocks
+      f32x16 s[2];
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb) {
+        s[kb] = f32x16{};
+        const int key = kb * 32 + qcol;
+#pragma unroll
+        for (int st = 0; st < DS; ++st) {
+          const int ch = 2 * st + half;
+          const bf16x8 ka = as_bf16x8(ld16(Ks + key * D + ((ch ^ k_swz(key)) * 8)));
+          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[st], s[kb], 0, 0, 0);
+        }
+      }
+      // mask: keys past the unit's range, and (causal) keys past the row's limit
+      const bool need_mask = (k0 + kBN > kv_hi) || (CAUSAL && k0 + kBN - 1 > wave_lim);
+      if (need_mask) {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
+            if (key >= kv_hi || (CAUSAL && key > lim)) s[kb][i] = -INFINITY;
+          }
+      }
+      // online softmax in base 2
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+      mx = xor32_max(mx);
+      const float m_new = fmaxf(m_run, mx * sl2);
+      const float m_use = m_new == -INFINITY ? 0.f : m_new;
+      const float alpha = fast_exp2(m_run - m_use);
+      float rs = 0.f;
+#pragma unroll
+      for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const float p = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -m_use));
+          s[kb][i] = p;
+          rs += p;
+        }
+      l_run = l_run * alpha + rs;
+      m_run = m_new;
+#pragma unroll
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+
+      // O^T += V^T . P^T, 16 keys per step
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int kb = u >> 1, i0 = 8 * (u & 1);
+        u32x4 pw;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) pw[w] = pack_bf16(s[kb][i0 + 2 * w], s[kb][i0 + 2 * w + 1]);
+        const bf16x8 pb = as_bf16x8(pw);
+#pragma unroll
+        for (int b = 0; b < DB; ++b) {
+          const int d = b * 32 + qcol;
+          const int ch = 2 * u + half;
+          const bf16x8 va = as_bf16x8(ld16(Vt + d * kBN + ((ch ^ vt_swz(d)) * 8)));
+          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[b], 0, 0, 0);
+        }
+      }
+    }
+    __syncthreads();
+  }
+
+  // ---- epilogue ------------------------------------------------------------
+  if (!wave_active) return;
+  const float l_tot = xor32_sum(l_run);
+  if (!row_ok) return;
+  const bool seen = l_tot > 0.f;
+  const float inv = seen ? 1.f / l_tot : 0.f;
+  const float lse = seen ? m_run + __log2f(l_tot) : -INFINITY;
+  if (prow < 0) {
+    const int64_t orow = static_cast<int64_t>(qo_begin + tok) * Hq + head;
+    if (a.out_fp32) {
+      float* op = static_cast<float*>(a.o) + orow * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = b * 32 + 8 * g + 4 * half;
+          *reinterpret_cast<f32x4*>(op + d0) =
+              f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
+        }
+    } else {
+      uint16_t* op = static_cast<uint16_t*>(a.o) + orow * D;
+#pragma unroll
+      for (int b = 0; b < DB; ++b)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          const int d0 = b * 32 + 8 * g + 4 * half;
+          u32x2 pk;
+          pk[0] = pack_bf16(o[b][4 * g] * inv, o[b][4 * g + 1] * inv);
+          pk[1] = pack_bf16(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
+          *reinterpret_cast<u32x2*>(op + d0) = pk;
+        }
+    }
+    if (a.lse && half == 0) a.lse[orow] = lse;
+  } else {
+    const int64_t prow_i = prow + (my_row - row_begin);
+    float* op = a.part_o + prow_i * D;
+#pragma unroll
+    for (int b = 0; b < DB; ++b)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const int d0 = b * 32 + 8 * g + 4 * half;
+        *reinterpret_cast<f32x4*>(op + d0) =
+            f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
+      }
+    if (half == 0) a.part_lse[prow_i] = lse;
+  }
+}
+
+template <int D, bool PAGED>
+hipError_t launch_prefill_d(const AttnArgs& a, bool causal, int grid, hipStream_t stream) {
+  if (causal)
+    prefill_kernel<D, PAGED, true><<<grid, kThreads, 0, stream>>>(a);
+  else
+    prefill_kernel<D, PAGED, false><<<grid, kThreads, 0, stream>>>(a);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool paged, bool causal, int grid,
+                          hipStream_t stream) {
+  if (grid <= 0) return hipSuccess;
+  if (head_dim == 128)
+    return paged ? launch_prefill_d<128, true>(a, causal, grid, stream)
+                 : launch_prefill_d<128, false>(a, causal, grid, stream);
+  return paged ? launch_prefill_d<64, true>(a, causal, grid, stream)
+               : launch_prefill_d<64, false>(a, causal, grid, stream);
+}
+
+}  // namespace pka

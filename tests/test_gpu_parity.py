@@ -1,0 +1,159 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle on
+the same seeded inputs, at sizes the oracle finishes in seconds that still
+span several tiles and ragged tails, plus the edge cases of the method."""
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_plan_amd as pka
+from paged_kv_cache_plan_amd import workloads as W
+from tests.gpu_common import compare, cuda, oracle_paged, run_paged, run_ragged
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("out_fp32", [False, True])
+def test_tiny_causal_paged(out_fp32):
+    w = W.tiny()
+    o, lse, info = run_paged(w, out_fp32=out_fp32)
+    ref_o, ref_l = oracle_paged(w)
+    compare(o, lse, ref_o, ref_l, "tiny")
+    assert info["kernel"] == pka.PKA_KERNEL_PREFILL
+
+
+def test_tiny_non_causal():
+    w = W.tiny(causal=False)
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), "tiny non-causal")
+
+
+@pytest.mark.parametrize("ps", [1, 3, 16, 64, 128])
+def test_page_sizes(ps):
+    w = W.gqa_append(seed=30 + ps, batch=3, prefix_range=(40, 400), chunk_range=(5, 150),
+                     page_size=ps)
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), f"ps={ps}")
+
+
+def test_dense_vs_vector_sparse_small():
+    w = W.dense_vs_sparse(batch=3, length=333, heads=4)
+    op, lp, _ = run_paged(w)
+    orr, lr, _ = run_ragged(w)
+    ref_o, ref_l = oracle.batch_attention_ragged(w.q, w.k, w.v, w.qo_indptr, w.kv_token_indptr,
+                                                 True, w.sm_scale)
+    compare(op, lp, ref_o, ref_l, "paged ps=1")
+    compare(orr, lr, ref_o, ref_l, "ragged")
+    # same values, same tiles: the two address policies give identical bits
+    assert torch.equal(op, orr) and torch.equal(lp, lr)
+
+
+def test_gqa_append_small():
+    w = W.gqa_append(batch=4, prefix_range=(512, 2048), chunk_range=(64, 300))
+    o, lse, info = run_paged(w)
+    compare(o, lse, *oracle_paged(w), "append")
+
+
+def test_long_causal_small():
+    w = W.long_causal(batch=1, length=2048)
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), "long causal 2048")
+
+
+def test_p5_shape():
+    w = W.p5_shape()
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), "h16 kv1 d128 ps64")
+
+
+@pytest.mark.parametrize("split", [True, False])
+def test_decode_small(split):
+    w = W.batch_decode(batch=16, kv_log2_range=(5.0, 12.0), kv_clamp=(1, 4096))
+    o, lse, info = run_paged(w, disable_split_kv=not split)
+    assert info["kernel"] == pka.PKA_KERNEL_DECODE
+    if split:
+        assert info["num_merge_groups"] > 0
+    else:
+        assert info["num_merge_groups"] == 0
+    compare(o, lse, *oracle_paged(w), f"decode split={split}")
+
+
+def test_decode_head_dim_64_and_mha():
+    w = W.batch_decode(seed=51, batch=6, kv_log2_range=(3.0, 10.0), kv_clamp=(1, 1024), head_dim=64,
+                       heads=8, kv_heads=8, page_size=4)
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), "decode D=64 MHA")
+
+
+def test_prefill_split_kv():
+    # few row blocks -> the planner splits the KV and merges afterwards
+    w = W.build("split", 7, [40], [3000], 8, 2, 128, 16, causal=True, pool_slack=0.1)
+    o, lse, info = run_paged(w)
+    assert info["num_merge_groups"] > 0
+    compare(o, lse, *oracle_paged(w), "prefill split")
+    o2, l2, info2 = run_paged(w, disable_split_kv=True)
+    assert info2["num_merge_groups"] == 0
+    compare(o2, l2, *oracle_paged(w), "prefill no split")
+
+
+def test_edge_cases():
+    # kv_len 0, qo_len 0, qo_len > kv_len (top rows see nothing), D=64
+    w = W.build("edge", 3, [3, 0, 70, 1], [0, 5, 20, 1], 4, 2, 64, 4, causal=True, pool_slack=0.5)
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), "edge")
+
+
+def test_plan_upload_bit_exact():
+    w = W.gqa_append(batch=5, prefix_range=(10, 900), chunk_range=(1, 200))
+    img, _ = pka.plan_host_image(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len,
+                                 w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, True,
+                                 w.num_pages)
+    plan = pka.Plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.num_qo_heads,
+                    w.num_kv_heads, w.head_dim, w.page_size, causal=True, num_pages=w.num_pages,
+                    device=cuda())
+    torch.cuda.synchronize()
+    dev_img = plan.int_ws[: img.numel() * 4].cpu().view(torch.int32)
+    assert torch.equal(dev_img, img)
+    plan.close()
+
+
+def test_debug_gather_bit_exact():
+    w = W.gqa_append(seed=8, batch=4, prefix_range=(10, 300), chunk_range=(1, 50), page_size=16)
+    plan = pka.Plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.num_qo_heads,
+                    w.num_kv_heads, w.head_dim, w.page_size, causal=True, num_pages=w.num_pages,
+                    device=cuda())
+    k, v = plan.debug_gather(w.paged_kv.to(cuda()))
+    torch.cuda.synchronize()
+    plan.close()
+    ks, vs = [], []
+    for r in range(w.batch):
+        pages = w.kv_indices[int(w.kv_indptr[r]):int(w.kv_indptr[r + 1])].long()
+        ks.append(w.paged_kv[pages, 0].reshape(-1, w.num_kv_heads, w.head_dim)[: w.kv_lens[r]])
+        vs.append(w.paged_kv[pages, 1].reshape(-1, w.num_kv_heads, w.head_dim)[: w.kv_lens[r]])
+    assert torch.equal(k.cpu().view(torch.int16), torch.cat(ks).view(torch.int16))
+    assert torch.equal(v.cpu().view(torch.int16), torch.cat(vs).view(torch.int16))
+
+
+def test_merge_states_kernel():
+    g = torch.Generator().manual_seed(0)
+    n, S, H, D = 37, 5, 3, 128
+    v = torch.randn(n, S, H, D, generator=g)
+    s = torch.randn(n, S, H, generator=g) * 4
+    s[0, :, 0] = float("-inf")
+    s[3, 1:, 2] = float("-inf")
+    ref_v, ref_s = oracle.merge_states(v, s)
+    vo, so = pka.merge_states(v.to(cuda()), s.to(cuda()), out_fp32=True)
+    torch.cuda.synchronize()
+    vo, so = vo.cpu(), so.cpu()
+    assert torch.equal(torch.isneginf(so), torch.isneginf(ref_s))
+    fin = torch.isfinite(ref_s)
+    assert (vo.double() - ref_v).abs().max() < 1e-5
+    assert (so.double()[fin] - ref_s[fin]).abs().max() < 1e-5
+    vb, _ = pka.merge_states(v.to(cuda()), s.to(cuda()), out_fp32=False)
+    assert (vb.float().cpu().double() - ref_v).abs().max() < 2e-2
+
+
+def test_deterministic():
+    w = W.batch_decode(seed=9, batch=8, kv_log2_range=(8.0, 12.0))
+    a = run_paged(w)
+    b = run_paged(w)
+    assert torch.equal(a[0], b[0]) and torch.equal(a[1], b[1])
