@@ -1,0 +1,293 @@
+#!/usr/bin/env python3
+"""Benchmark of paged-KV batch attention on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+
+A step is one run of the planned batch (every kernel the plan launches:
+attention, and the split-KV merge when the plan split any KV) over inputs
+already resident in HBM; the plan is made once beforehand, as a serving
+engine plans a batch once and runs it for every layer.  Host planning time
+is reported separately as plan_ms.
+
+The JSON line's value is the causal paged prefill throughput on the
+dense-vs-vector-sparse workload (B=16, L=1024, Hq=Hkv=32, D=128,
+page_size=1, randomly permuted pages), the comparison the FlashInfer 0.2
+release blog benchmarks.  The same run also reports the ragged dense
+baseline, GQA append-prefill, long-context causal prefill (compute-bound)
+and batch decode (HBM-bound) under "workloads".
+
+Throughput uses algorithmic work only: prefill flops = 4 D Hq (visible
+query-key pairs); decode bytes = every valid K/V row once + q + o + lse +
+page ids.  Two input copies alternate between steps so that no step finds
+its K/V left in the 256 MB last-level cache by the previous one.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
+METRIC = "causal paged prefill TFLOP/s (D=128) and decode HBM GB/s, % of roofline"
+KERNEL_SOURCES = ["prefill.hip", "decode.hip", "merge.hip", "device.h", "args.h"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_plan_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def prefill_flops(w) -> float:
+    import paged_kv_cache_plan_amd as pka
+    return 4.0 * w.head_dim * w.num_qo_heads * pka.visible_pairs(w.qo_lens, w.kv_lens, w.causal)
+
+
+def decode_bytes(w) -> float:
+    kv = sum(w.kv_lens) * 2 * w.num_kv_heads * w.head_dim * 2
+    q = w.total_q * w.num_qo_heads * w.head_dim * 2
+    o = q
+    lse = w.total_q * w.num_qo_heads * 4
+    idx = w.nnz_pages * 4
+    return float(kv + q + o + lse + idx)
+
+
+def make_plan(w, dev, ragged=False):
+    import torch
+    import paged_kv_cache_plan_amd as pka
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    if ragged:
+        plan = pka.Plan(w.qo_indptr, w.kv_token_indptr, None, None, w.num_qo_heads, w.num_kv_heads,
+                        w.head_dim, 1, causal=w.causal, sm_scale=w.sm_scale, ragged=True, device=dev)
+    else:
+        plan = pka.Plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.num_qo_heads,
+                        w.num_kv_heads, w.head_dim, w.page_size, causal=w.causal, sm_scale=w.sm_scale,
+                        num_pages=w.num_pages, device=dev)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    torch.cuda.synchronize()
+    return plan, plan_ms
+
+
+def time_launches(launch, steps, warmup):
+    """Warm up, then time exactly `steps` launches bracketed by synchronisation.
+    Returns (total ms, per-launch ms list) from HIP events recorded on the
+    stream the library launches on (torch's current stream)."""
+    import torch
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    start.record()
+    for i in range(steps):
+        evs[i][0].record()
+        launch(i)
+        evs[i][1].record()
+    end.record()
+    torch.cuda.synchronize()
+    return start.elapsed_time(end), [a.elapsed_time(b) for a, b in evs]
+
+
+def bench_workload(name, w, dev, steps, warmup, ragged=False, copies=2):
+    import torch
+    plan, plan_ms = make_plan(w, dev, ragged)
+    qs = [w.q] + [w.q.clone() for _ in range(copies - 1)]
+    if ragged:
+        ks = [w.k] + [w.k.clone() for _ in range(copies - 1)]
+        vs = [w.v] + [w.v.clone() for _ in range(copies - 1)]
+    else:
+        pools = [w.paged_kv] + [w.paged_kv.clone() for _ in range(copies - 1)]
+    o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.total_q, w.num_qo_heads), dtype=torch.float32, device=dev)
+
+    def launch(i):
+        c = i % copies
+        if ragged:
+            plan.run_ragged(qs[c], ks[c], vs[c], o, lse)
+        else:
+            plan.run(qs[c], pools[c], o, lse)
+
+    total_ms, per = time_launches(launch, steps, warmup)
+    info = plan.info
+    plan.close()
+    per_sorted = sorted(per)
+    med = per_sorted[len(per) // 2]
+    avg = sum(per) / len(per)
+    res = {"ms_per_step": total_ms / steps, "launch_ms_avg": avg, "launch_ms_median": med,
+           "launch_ms_min": per_sorted[0], "plan_ms": plan_ms, "units": info["num_units"],
+           "merge_groups": info["num_merge_groups"], "kv_chunk": info["kv_chunk"],
+           "kernel": "decode" if info["kernel"] == 1 else "prefill"}
+    if info["kernel"] == 1:
+        b = decode_bytes(w)
+        res.update({"algorithmic_bytes": b, "GB_per_s": b / (avg * 1e-3) / 1e9,
+                    "frac_of_hbm_peak": b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS})
+    else:
+        f = prefill_flops(w)
+        res.update({"algorithmic_flops": f, "TFLOP_per_s": f / (avg * 1e-3) / 1e12,
+                    "frac_of_bf16_peak": f / (avg * 1e-3) / 1e12 / PEAK_BF16_TFLOPS})
+    del qs, o, lse
+    if ragged:
+        del ks, vs
+    else:
+        del pools
+    torch.cuda.empty_cache()
+    return res
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The CPU fp64 oracle, as it stands, on a bounded sample of the headline
+    workload (the same inputs the GPU was timed on, copied to the host):
+    whole requests (all heads, all rows) until ~budget_s seconds."""
+    import torch
+
+    import oracle
+    import paged_kv_cache_plan_amd as pka
+    threads = torch.get_num_threads()
+    w.q, w.paged_kv = w.q.cpu(), w.paged_kv.cpu()
+    done, flops, t_total = 0, 0.0, 0.0
+    while done < w.batch and t_total < budget_s:
+        q0, q1 = int(w.qo_indptr[done]), int(w.qo_indptr[done + 1])
+        t0 = time.perf_counter()
+        oracle.batch_attention_paged(w.q, w.paged_kv, w.qo_indptr, w.kv_indptr, w.kv_indices,
+                                     w.kv_last_page_len, True, w.sm_scale, rows=list(range(q0, q1)))
+        t_total += time.perf_counter() - t0
+        flops += 4.0 * w.head_dim * w.num_qo_heads * pka.visible_pairs([q1 - q0], [w.kv_lens[done]], True)
+        done += 1
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"{done} of {w.batch} requests (all {w.num_qo_heads} heads, all rows) of the "
+                      f"dense-vs-vector-sparse workload, paged page_size=1, fp64 torch CPU, "
+                      f"{t_total:.1f} s", "os_cpu_count": os.cpu_count()}
+
+
+def load_traffic():
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        t = json.load(f)
+    if t.get("kernel_source_hash") != kernel_source_hash():
+        return None  # kernel changed since the counters were taken
+    return t
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None,
+                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5 (profiling runs)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (counter calibration)")
+    args = ap.parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this library has no multi-GPU path "
+              "(see the sharding notes); run with --gpus 1", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    import paged_kv_cache_plan_amd as pka
+    from paged_kv_cache_plan_amd import workloads as W
+    pka.load_library()
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    if args.copy_calibration:
+        src = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes": src.numel() * 4}))
+        return
+
+    prop = torch.cuda.get_device_properties(dev)
+    sel = args.only
+    results = {}
+
+    def want(n):
+        return sel is None or sel == n
+
+    w2 = None
+    if want("c2_paged") or want("c2_ragged"):
+        w2 = W.dense_vs_sparse(device=dev)
+        if want("c2_paged"):
+            results["dense_vs_sparse_paged_ps1"] = bench_workload("c2_paged", w2, dev, args.steps, args.warmup)
+            print(f"# c2 paged: {results['dense_vs_sparse_paged_ps1']}", file=sys.stderr, flush=True)
+        if want("c2_ragged"):
+            results["dense_vs_sparse_ragged"] = bench_workload("c2_ragged", w2, dev, args.steps, args.warmup,
+                                                               ragged=True)
+            print(f"# c2 ragged: {results['dense_vs_sparse_ragged']}", file=sys.stderr, flush=True)
+        w2.k = w2.v = None
+    if want("c3"):
+        w3 = W.gqa_append(device=dev)
+        results["gqa_append"] = bench_workload("c3", w3, dev, args.steps, args.warmup)
+        print(f"# c3: {results['gqa_append']}", file=sys.stderr, flush=True)
+        del w3
+    if want("c4"):
+        w4 = W.long_causal(device=dev)
+        results["long_causal"] = bench_workload("c4", w4, dev, args.steps, args.warmup)
+        print(f"# c4: {results['long_causal']}", file=sys.stderr, flush=True)
+        del w4
+    if want("c5"):
+        w5 = W.batch_decode(device=dev)
+        results["batch_decode"] = bench_workload("c5", w5, dev, args.steps, args.warmup)
+        print(f"# c5: {results['batch_decode']}", file=sys.stderr, flush=True)
+        del w5
+    torch.cuda.empty_cache()
+
+    if sel is not None:
+        print(json.dumps({"only": sel, "results": results}))
+        return
+
+    main_r = results["dense_vs_sparse_paged_ps1"]
+    rag = results["dense_vs_sparse_ragged"]
+    traffic = load_traffic()
+    roofline = {"bound": "mfma", "achieved": main_r["TFLOP_per_s"], "peak": PEAK_BF16_TFLOPS,
+                "unit": "TFLOP/s", "frac": main_r["TFLOP_per_s"] / PEAK_BF16_TFLOPS,
+                "traffic": traffic.get("c2_paged_bytes_per_launch") if traffic else None,
+                "kernel": "prefill_kernel<128, paged, causal>",
+                "per_launch_flops": main_r["algorithmic_flops"], "avg_launch_ms": main_r["launch_ms_avg"]}
+    line = {
+        "metric": METRIC,
+        "value": main_r["TFLOP_per_s"],
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": main_r["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "dense_vs_vector_sparse causal paged prefill: B=16, L=1024, Hq=Hkv=32, "
+                               "D=128, page_size=1, randomly permuted pages",
+                   "batch": 16, "seq_len": 1024, "num_qo_heads": 32, "num_kv_heads": 32, "head_dim": 128,
+                   "page_size": 1, "parallelism": "single GPU"},
+        "roofline": roofline,
+        "paged_over_ragged": main_r["TFLOP_per_s"] / rag["TFLOP_per_s"],
+        "device": {"name": prop.name, "compute_units": prop.multi_processor_count,
+                   "clock_khz": getattr(prop, "clock_rate", None)},
+        "workloads": results,
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(w2)
+    print(json.dumps(line))
+
+
+if __name__ == "__main__":
+    main()

@@ -20,6 +20,8 @@
 //   O^T     += V^T . P^T.
 // The kernel is bound by HBM bandwidth; the MFMA padding of G < 16 heads to
 // 16 columns costs matrix-core time that is otherwise idle.
+#include <type_traits>
+
 #include "args.h"
 #include "device.h"
 #include "launch.h"
@@ -34,8 +36,15 @@ constexpr int kThreads = 64 * kWaves;
 // V^T row chunk swizzle (4 chunks of 8 keys per 32-key row).
 __device__ __forceinline__ int dvt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3; }
 
-template <int D, bool PAGED>
+// How a step finds its K/V rows: ragged dense tensors, a page table whose
+// page_size is a power of two >= 16 (each 16-key half of a step lies in one
+// page, so the whole wave shares two page ids), or any other page table (one
+// page id per row).
+enum IdMode : int { kRagged = 0, kPagedUniform = 1, kPagedLane = 2 };
+
+template <int D, int MODE>
 __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+  constexpr bool PAGED = MODE != kRagged;
   constexpr int CPR = D / 8;   // 16-byte chunks per row
   constexpr int DS = D / 32;   // k-steps of the S^T MFMA
   constexpr int DB = D / 16;   // 16-row d blocks of O^T
@@ -47,7 +56,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int32_t* unit = a.units + static_cast<int64_t>(blockIdx.x) * 8;
   const int r = unit[0], hk = unit[1];
   const int kv_lo = unit[4], kv_hi = unit[5], prow = unit[6];
@@ -67,16 +76,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   }
 
   const int ps = a.page_size, pshift = a.page_shift;
-  auto row_off = [&](int key) -> int64_t {  // element offset of the K row of `key`
-    if constexpr (PAGED) {
-      const int pg = pshift >= 0 ? (key >> pshift) : (key / ps);
-      const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
-      return static_cast<int64_t>(a.kv_indices[kv_base + pg]) * a.page_stride +
-             static_cast<int64_t>(slot) * a.row_stride;
-    } else {
-      return static_cast<int64_t>(kv_base + key) * a.row_stride;
-    }
-  };
+  constexpr bool scalar_ids = MODE == kPagedUniform;
   const uint16_t* kb_ptr = a.k + hk * D;
   const uint16_t* vb_ptr = PAGED ? kb_ptr + a.v_offset : a.v + hk * D;
 
@@ -85,35 +85,92 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   const bool v_lane = vg < 4;
   uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * VT_ELEMS;
 
+  // Keys of one step handled by this lane: K rows 16 kb + col (kb = 0, 1);
+  // V rows for slot 8 vg + j: 4 vg + j (j < 4), 16 + 4 vg + j - 4 (j >= 4).
+  auto v_key = [&](int j) { return j < 4 ? 4 * vg + j : 16 + 4 * vg + (j - 4); };
+
+  // Page ids of a step.
+  struct IdsUniform { int s[2]; };
+  struct IdsLane { int k[2]; int v[8]; };
+  struct IdsNone {};
+  using Ids = typename std::conditional<MODE == kPagedUniform, IdsUniform,
+                typename std::conditional<MODE == kPagedLane, IdsLane, IdsNone>::type>::type;
+  auto fetch_ids = [&](int k0, Ids& id) {
+    if constexpr (MODE == kPagedUniform) {
+      id.s[0] = a.kv_indices[kv_base + (k0 >> pshift)];
+      id.s[1] = (k0 + 16 < kv_hi) ? a.kv_indices[kv_base + ((k0 + 16) >> pshift)] : id.s[0];
+    } else if constexpr (MODE == kPagedLane) {
+      {
+#pragma unroll
+        for (int kb = 0; kb < 2; ++kb) {
+          const int key = k0 + 16 * kb + col;
+          id.k[kb] = key < kv_hi ? a.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const int key = k0 + v_key(j);
+          id.v[j] = (v_lane && key < kv_hi) ? a.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
+        }
+      }
+    }
+  };
+  auto row_off = [&](int key, int pid) -> int64_t {  // element offset of the K row of `key`
+    if constexpr (PAGED) {
+      const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
+      return static_cast<int64_t>(pid) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride;
+    } else {
+      return static_cast<int64_t>(kv_base + key) * a.row_stride;
+    }
+  };
+  struct Data { u32x4 k[2][DS]; u32x4 v[8]; };
+  auto fetch_data = [&](int k0, const Ids& id, Data& x) {
+#pragma unroll
+    for (int kb = 0; kb < 2; ++kb) {
+      const int key = k0 + 16 * kb + col;
+      int pid = 0;
+      if constexpr (MODE == kPagedUniform) pid = id.s[kb];
+      if constexpr (MODE == kPagedLane) pid = id.k[kb];
+      if (key < kv_hi) {
+        const uint16_t* p = kb_ptr + row_off(key, pid) + 8 * g4;
+#pragma unroll
+        for (int s = 0; s < DS; ++s) x.k[kb][s] = ld16(p + 32 * s);
+      } else {
+#pragma unroll
+        for (int s = 0; s < DS; ++s) x.k[kb][s] = u32x4{0, 0, 0, 0};
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int key = k0 + v_key(j);
+      int pid = 0;
+      if constexpr (MODE == kPagedUniform) pid = id.s[j >> 2];
+      if constexpr (MODE == kPagedLane) pid = id.v[j];
+      x.v[j] = (v_lane && key < kv_hi) ? ld16(vb_ptr + row_off(key, pid) + 8 * vc) : u32x4{0, 0, 0, 0};
+    }
+  };
+
   f32x4 o[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) o[b] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
 
+  // Steps t = wave, wave + 4, ...: page ids two steps ahead, data one ahead.
   const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kTK - 1) / kTK : 0;
-  for (int t = wave; t < n_tiles; t += kWaves) {
+  Ids ids_next{};
+  Data cur{}, nxt{};
+  int t = wave;
+  if (t < n_tiles) {
+    Ids ids0{};
+    fetch_ids(kv_lo + t * kTK, ids0);
+    fetch_data(kv_lo + t * kTK, ids0, cur);
+    if (t + kWaves < n_tiles) fetch_ids(kv_lo + (t + kWaves) * kTK, ids_next);
+  }
+  for (; t < n_tiles; t += kWaves) {
     const int k0 = kv_lo + t * kTK;
-    // K operand: keys k0 + 16 kb + col, d = 32 s + 8 g4 .. + 8
-    u32x4 ka[2][DS];
-#pragma unroll
-    for (int kb = 0; kb < 2; ++kb) {
-      const int key = k0 + 16 * kb + col;
-      if (key < kv_hi) {
-        const uint16_t* p = kb_ptr + row_off(key) + 8 * g4;
-#pragma unroll
-        for (int s = 0; s < DS; ++s) ka[kb][s] = ld16(p + 32 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < DS; ++s) ka[kb][s] = u32x4{0, 0, 0, 0};
-      }
-    }
-    // V rows for slots 8 vg + j: key 4 vg + j (j < 4), 16 + 4 vg + j - 4 (j >= 4)
-    u32x4 vv[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int key = k0 + (j < 4 ? 4 * vg + j : 16 + 4 * vg + (j - 4));
-      vv[j] = (v_lane && key < kv_hi) ? ld16(vb_ptr + row_off(key) + 8 * vc) : u32x4{0, 0, 0, 0};
+    if (t + kWaves < n_tiles) {
+      fetch_data(k0 + kWaves * kTK, ids_next, nxt);
+      if (t + 2 * kWaves < n_tiles) fetch_ids(k0 + 2 * kWaves * kTK, ids_next);
     }
 
     f32x4 s[2];
@@ -122,7 +179,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       s[kb] = f32x4{};
 #pragma unroll
       for (int st = 0; st < DS; ++st)
-        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(ka[kb][st]), qreg[st], s[kb], 0, 0, 0);
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(cur.k[kb][st]), qreg[st], s[kb], 0, 0, 0);
     }
 
     // transpose V into the wave's V^T tile
@@ -135,7 +192,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
         u32x4 pk;
 #pragma unroll
         for (int h = 0; h < 4; ++h)
-          pk[h] = (e & 1) ? pack_hi16(vv[2 * h][w], vv[2 * h + 1][w]) : pack_lo16(vv[2 * h][w], vv[2 * h + 1][w]);
+          pk[h] = (e & 1) ? pack_hi16(cur.v[2 * h][w], cur.v[2 * h + 1][w])
+                          : pack_lo16(cur.v[2 * h][w], cur.v[2 * h + 1][w]);
         st16(vt + d * kTK + ((vg ^ dvt_swz(d)) * 8), pk);
       }
     }
@@ -170,8 +228,10 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       }
     l_run = l_run * alpha + rs;
     m_run = m_new;
+    if (__any(alpha != 1.f)) {
 #pragma unroll
-    for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+    }
 
     u32x4 pw;
     pw[0] = pack_bf16(s[0][0], s[0][1]);
@@ -185,6 +245,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       const bf16x8 va = as_bf16x8(ld16(vt + d * kTK + ((g4 ^ dvt_swz(d)) * 8)));
       o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[b], 0, 0, 0);
     }
+    cur = nxt;
   }
 
   // ---- merge the four waves' states -------------------------------------
@@ -236,10 +297,12 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 
 template <int D>
 hipError_t launch_decode_d(const AttnArgs& a, bool paged, int grid, hipStream_t stream) {
-  if (paged)
-    decode_kernel<D, true><<<grid, kThreads, 0, stream>>>(a);
+  if (!paged)
+    decode_kernel<D, kRagged><<<grid, kThreads, 0, stream>>>(a);
+  else if (a.page_shift >= 4)
+    decode_kernel<D, kPagedUniform><<<grid, kThreads, 0, stream>>>(a);
   else
-    decode_kernel<D, false><<<grid, kThreads, 0, stream>>>(a);
+    decode_kernel<D, kPagedLane><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

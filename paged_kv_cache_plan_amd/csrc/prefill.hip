@@ -44,8 +44,10 @@ __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~15) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
 }
 // 16-byte chunk swizzles (XOR), chosen so that the MFMA operand reads are
-// bank-conflict free: K rows by key, V^T rows by d.
-__device__ __forceinline__ int k_swz(int key) { return key & 7; }
+// bank-conflict free for 16 lanes per LDS cycle: K rows by key (all chunks
+// of a row), V^T rows by d.
+template <int CPR>
+__device__ __forceinline__ int k_swz(int key) { return key & (CPR - 1); }
 __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 template <int D, bool PAGED, bool CAUSAL>
@@ -61,7 +63,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wave = tid >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
   const int32_t* unit = a.units + static_cast<int64_t>(blockIdx.x) * 8;
   const int r = unit[0], hk = unit[1], row_begin = unit[2], row_end = unit[3];
   const int kv_lo = unit[4], kv_hi = unit[5], prow = unit[6];
@@ -99,31 +101,39 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
 
   auto fetch_ids = [&](int k0, int* ids) {
     if constexpr (PAGED) {
+      const bool full = k0 + kBN <= kv_hi;  // uniform
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         const int key = k0 + KPT * lj + i;
         const int pg = pshift >= 0 ? (key >> pshift) : (key / ps);
-        ids[i] = key < kv_hi ? a.kv_indices[kv_base + pg] : 0;
+        int id = 0;
+        if (full || key < kv_hi) id = a.kv_indices[kv_base + pg];
+        ids[i] = id;
       }
     }
   };
+  auto fetch_one = [&](int key, int id, int i) {
+    int64_t off;
+    if constexpr (PAGED) {
+      const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
+      off = static_cast<int64_t>(id) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride;
+    } else {
+      off = static_cast<int64_t>(kv_base + key) * a.row_stride;
+    }
+    kreg[i] = ld16(kbase + off);
+    vreg[i] = ld16(vbase + off);
+  };
   auto fetch_data = [&](int k0, const int* ids) {
+    if (k0 + kBN <= kv_hi) {  // uniform: the whole tile is in range
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int key = k0 + KPT * lj + i;
-      if (key < kv_hi) {
-        int64_t off;
-        if constexpr (PAGED) {
-          const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
-          off = static_cast<int64_t>(ids[i]) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride;
-        } else {
-          off = static_cast<int64_t>(kv_base + key) * a.row_stride;
-        }
-        kreg[i] = ld16(kbase + off);
-        vreg[i] = ld16(vbase + off);
-      } else {
+      for (int i = 0; i < KPT; ++i) fetch_one(k0 + KPT * lj + i, ids[i], i);
+    } else {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const int key = k0 + KPT * lj + i;
         kreg[i] = u32x4{0, 0, 0, 0};
         vreg[i] = u32x4{0, 0, 0, 0};
+        if (key < kv_hi) fetch_one(key, ids[i], i);
       }
     }
   };
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int key = KPT * lj + i;
-      st16(Ks + key * D + ((lc ^ k_swz(key)) * 8), kreg[i]);
+      st16(Ks + key * D + ((lc ^ k_swz<CPR>(key)) * 8), kreg[i]);
     }
     const int p0 = vt_pos(KPT * lj);
 #pragma unroll
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
 #pragma unroll
         for (int st = 0; st < DS; ++st) {
           const int ch = 2 * st + half;
-          const bf16x8 ka = as_bf16x8(ld16(Ks + key * D + ((ch ^ k_swz(key)) * 8)));
+          const bf16x8 ka = as_bf16x8(ld16(Ks + key * D + ((ch ^ k_swz<CPR>(key)) * 8)));
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[st], s[kb], 0, 0, 0);
         }
       }
@@ -220,8 +230,10 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
         }
       l_run = l_run * alpha + rs;
       m_run = m_new;
+      if (__any(alpha != 1.f)) {  // the running max moved for some row of this wave
 #pragma unroll
-      for (int b = 0; b < DB; ++b) o[b] *= alpha;
+        for (int b = 0; b < DB; ++b) o[b] *= alpha;
+      }
 
       // O^T += V^T . P^T, 16 keys per step
 #pragma unroll

@@ -17,10 +17,14 @@ sparsity"; flashinfer-trace discussion #15, "Notes on fa3_gqa_prefill_v1"):
 * ragged dense K/V ``k, v`` bf16 ``[total_kv, Hkv, D]`` with token offsets
   ``kv_token_indptr[B+1]`` (only built where the workload asks for it).
 
-Every random draw uses ``torch.Generator('cpu').manual_seed(seed)`` in a fixed
-order: lengths -> page permutation -> Q -> K/V -> poison.  Values are fp32
-N(0, 1) rounded to bf16.  Large tensors are drawn in fixed-size chunks so that
-host memory stays bounded; the chunk size is part of the recipe.
+Every random draw is seeded, in a fixed order: lengths -> page permutation ->
+Q -> K/V -> poison.  Lengths and page permutations always come from
+``torch.Generator('cpu').manual_seed(seed)``.  Q and K/V values are fp32
+N(0, 1) rounded to bf16, drawn on ``device``: with the default ``device='cpu'``
+they continue the same CPU generator; with a GPU device they come from
+``torch.Generator(device).manual_seed(seed)`` on that device (multi-GB pools
+would take minutes on the host).  Large tensors are drawn in fixed-size chunks
+so that memory stays bounded; the chunk size is part of the recipe.
 
 Unused pool pages and the slots past ``kv_last_page_len`` in each last page are
 filled with NaN ("poison") wherever the workload enables it: a kernel that reads
@@ -74,15 +78,17 @@ class Workload:
 
 
 def _randn_bf16(shape, gen) -> torch.Tensor:
-    """fp32 N(0,1) draws rounded to bf16, drawn in fixed-size chunks."""
+    """fp32 N(0,1) draws rounded to bf16, drawn in fixed-size chunks on the
+    generator's device."""
     n = 1
     for s in shape:
         n *= int(s)
-    out = torch.empty(n, dtype=torch.bfloat16)
+    out = torch.empty(n, dtype=torch.bfloat16, device=gen.device)
     pos = 0
     while pos < n:
         m = min(_DRAW_CHUNK, n - pos)
-        out[pos:pos + m] = torch.randn(m, generator=gen, dtype=torch.float32).to(torch.bfloat16)
+        out[pos:pos + m] = torch.randn(m, generator=gen, dtype=torch.float32,
+                                       device=gen.device).to(torch.bfloat16)
         pos += m
     return out.view(*shape)
 
@@ -111,8 +117,8 @@ def page_table_for(kv_lens, page_size, num_pages, gen):
 def _poison(paged_kv, kv_indptr, kv_indices, kv_last_page_len, page_size):
     """NaN-fill every pool slot the page table does not reference."""
     num_pages = paged_kv.shape[0]
-    used = torch.zeros(num_pages, dtype=torch.bool)
-    used[kv_indices.long()] = True
+    used = torch.zeros(num_pages, dtype=torch.bool, device=paged_kv.device)
+    used[kv_indices.long().to(paged_kv.device)] = True
     paged_kv[~used] = float("nan")
     B = kv_last_page_len.numel()
     for r in range(B):
@@ -126,7 +132,7 @@ def _poison(paged_kv, kv_indptr, kv_indices, kv_last_page_len, page_size):
 
 def build(name, seed, qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim,
           page_size, causal=True, pool_slack=0.0, poison=True, ragged=False,
-          gen=None, notes=None, num_pages=None) -> Workload:
+          gen=None, notes=None, num_pages=None, device="cpu") -> Workload:
     """Assemble a workload from explicit lengths.
 
     Draw order after the lengths: page permutation -> Q -> K/V -> poison.
@@ -147,24 +153,26 @@ def build(name, seed, qo_lens, kv_lens, num_qo_heads, num_kv_heads, head_dim,
                              dtype=torch.int32)
     total_q = int(qo_indptr[-1])
     H, Hk, D = num_qo_heads, num_kv_heads, head_dim
-    q = _randn_bf16((total_q, H, D), gen)
+    dev = torch.device(device)
+    vgen = gen if dev.type == "cpu" else torch.Generator(device=dev).manual_seed(seed)
+    q = _randn_bf16((total_q, H, D), vgen)
     k = v = kv_tok = None
     if ragged:
         total_kv = sum(kv_lens)
         kv_tok = torch.tensor([0] + list(torch.tensor(kv_lens).cumsum(0).tolist()),
                               dtype=torch.int32)
-        k = _randn_bf16((total_kv, Hk, D), gen)
-        v = _randn_bf16((total_kv, Hk, D), gen)
-        paged_kv = torch.zeros((num_pages, 2, ps, Hk, D), dtype=torch.bfloat16)
+        k = _randn_bf16((total_kv, Hk, D), vgen)
+        v = _randn_bf16((total_kv, Hk, D), vgen)
+        paged_kv = torch.zeros((num_pages, 2, ps, Hk, D), dtype=torch.bfloat16, device=dev)
         for r in range(B):
             t0, L = int(kv_tok[r]), kv_lens[r]
             t = torch.arange(L)
-            page = kv_indices[int(kv_indptr[r]) + t // ps].long()
-            slot = t % ps
+            page = kv_indices[int(kv_indptr[r]) + t // ps].long().to(dev)
+            slot = (t % ps).to(dev)
             paged_kv[page, 0, slot] = k[t0:t0 + L]
             paged_kv[page, 1, slot] = v[t0:t0 + L]
     else:
-        paged_kv = _randn_bf16((num_pages, 2, ps, Hk, D), gen)
+        paged_kv = _randn_bf16((num_pages, 2, ps, Hk, D), vgen)
     if poison:
         _poison(paged_kv, kv_indptr, kv_indices, last, ps)
     return Workload(
