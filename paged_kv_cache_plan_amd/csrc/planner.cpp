@@ -193,12 +193,61 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   }
   if (units.size() > size_t(1) << 30) return fail(err, kUnsupported, "too many work units");
 
-  // Longest-first order: the hardware hands out workgroups roughly in index
-  // order, so big units start first and small ones fill the tail.
-  std::stable_sort(units.begin(), units.end(), [](const Unit& a, const Unit& b) {
+  auto longest_first = [](const Unit& a, const Unit& b) {
     if (a.cost != b.cost) return a.cost > b.cost;
     return a.seq < b.seq;
-  });
+  };
+  if (decode || in.num_xcds <= 1 || units.size() <= static_cast<size_t>(in.num_xcds)) {
+    // Longest-first order: the hardware hands out workgroups roughly in index
+    // order, so big units start first and small ones fill the tail.
+    std::stable_sort(units.begin(), units.end(), longest_first);
+  } else {
+    // Prefill: the units of one (request, kv head) read the same K/V, so keep
+    // them on one XCD (workgroup b runs on XCD b % num_xcds) and close in
+    // time, for reuse in that XCD's L2.  Groups go to XCDs longest-first onto
+    // the least loaded queue; each queue runs its groups in that order and
+    // each group's units longest-first.  Queues are padded with empty units
+    // (no rows, no keys) to equal length so the b % num_xcds mapping holds.
+    struct Grp { int64_t cost; size_t first, count; };
+    std::vector<Grp> grps;
+    for (size_t i = 0; i < units.size();) {
+      size_t j = i;
+      int64_t c = 0;
+      while (j < units.size() && units[j].f[kUnitRequest] == units[i].f[kUnitRequest] &&
+             units[j].f[kUnitKvHead] == units[i].f[kUnitKvHead]) {
+        c += units[j].cost;
+        ++j;
+      }
+      grps.push_back({c, i, j - i});
+      i = j;
+    }
+    std::vector<size_t> order(grps.size());
+    std::iota(order.begin(), order.end(), size_t(0));
+    std::stable_sort(order.begin(), order.end(),
+                     [&](size_t a, size_t b) { return grps[a].cost > grps[b].cost; });
+    const int X = in.num_xcds;
+    std::vector<std::vector<Unit>> queue(X);
+    std::vector<int64_t> load(X, 0);
+    for (size_t gi : order) {
+      int x = 0;
+      for (int k = 1; k < X; ++k)
+        if (load[k] < load[x]) x = k;
+      load[x] += grps[gi].cost;
+      std::vector<Unit> g(units.begin() + grps[gi].first, units.begin() + grps[gi].first + grps[gi].count);
+      std::stable_sort(g.begin(), g.end(), longest_first);
+      queue[x].insert(queue[x].end(), g.begin(), g.end());
+    }
+    size_t len = 0;
+    for (const auto& q : queue) len = std::max(len, q.size());
+    Unit empty{};
+    empty.f[kUnitPartialRow] = -1;
+    empty.cost = 0;
+    std::vector<Unit> out;
+    out.reserve(len * X);
+    for (size_t i = 0; i < len; ++i)
+      for (int x = 0; x < X; ++x) out.push_back(i < queue[x].size() ? queue[x][i] : empty);
+    units.swap(out);
+  }
 
   // Assemble the image.
   const int32_t n_units = static_cast<int32_t>(units.size());

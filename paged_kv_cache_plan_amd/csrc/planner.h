@@ -106,6 +106,7 @@ struct PlanInput {
   bool check_indices = true;   // validate kv_indices (needs the array)
   int32_t kv_chunk_override = 0;  // >0: keys per split chunk (tuning); 0: heuristic
   int32_t num_cus = 256;          // compute units the split heuristic aims to fill
+  int32_t num_xcds = 8;           // XCDs workgroups are dealt to round-robin (prefill order)
 };
 
 struct PlanResult {

@@ -1,0 +1,335 @@
+"""CPU tests of the host planner and the C ABI (no GPU needed).
+
+* every symbol include/pka.h declares is exported by libpka.so;
+* coverage: every visible (request, query head, query row, key) lies in
+  exactly one work unit, and no unit reads a key at or past kv_len;
+* merge groups and partial rows are consistent;
+* the plan is deterministic and its bytes equal a Python re-statement of the
+  planning rule (tiling, split choice, ordering, image layout);
+* invalid inputs return error codes with a message, never abort.
+"""
+import ctypes
+import os
+import random
+import re
+
+import pytest
+import torch
+
+import paged_kv_cache_plan_amd as pka
+from paged_kv_cache_plan_amd import workloads as W
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+# Planner constants (paged_kv_cache_plan_amd/csrc/planner.h).
+BLOCK_ROWS, BLOCK_KEYS, DECODE_TILE, DECODE_MAX_G = 128, 64, 32, 16
+NUM_CUS, NUM_XCDS = 256, 8
+UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 8, 8, 8
+
+
+def test_library_exports_every_declared_symbol():
+    header = open(os.path.join(ROOT, "include", "pka.h")).read()
+    declared = set(re.findall(r"\b(pka_[a-z_]+)\s*\(", header))
+    assert declared == set(pka.EXPORTED), declared ^ set(pka.EXPORTED)
+    lib = pka.load_library()
+    for name in sorted(declared):
+        assert hasattr(lib, name), name
+
+
+# ---------------------------------------------------------------------------
+# Python re-statement of the planning rule
+# ---------------------------------------------------------------------------
+
+def _cdiv(a, b):
+    return -(-a // b)
+
+
+def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, flags, ragged=False):
+    B = len(qo_indptr) - 1
+    G = Hq // Hkv
+    qo_len = [qo_indptr[r + 1] - qo_indptr[r] for r in range(B)]
+    if ragged:
+        kv_len = [kv_indptr[r + 1] - kv_indptr[r] for r in range(B)]
+    else:
+        kv_len = [0 if kv_indptr[r + 1] == kv_indptr[r] else
+                  (kv_indptr[r + 1] - kv_indptr[r] - 1) * ps + last[r] for r in range(B)]
+    decode = B > 0 and max(qo_len) <= 1 and G <= DECODE_MAX_G
+    blocks = []
+    if decode:
+        rows_per = G
+        for r in range(B):
+            if qo_len[r]:
+                blocks += [(r, hk, 0, G, kv_len[r]) for hk in range(Hkv)]
+    else:
+        rows_per = BLOCK_ROWS
+        for r in range(B):
+            if not qo_len[r]:
+                continue
+            rows = qo_len[r] * G
+            for hk in range(Hkv):
+                for r0 in range(0, rows, BLOCK_ROWS):
+                    r1 = min(rows, r0 + BLOCK_ROWS)
+                    hi = kv_len[r]
+                    if causal:
+                        hi = max(0, min(hi, (r1 - 1) // G + kv_len[r] - qo_len[r] + 1))
+                    blocks.append((r, hk, r0, r1, hi))
+    chunk = 0
+    if not (flags & pka.PKA_DISABLE_SPLIT_KV) and blocks:
+        if decode:
+            keys = sum(b[4] for b in blocks)
+            chunk = _cdiv(keys, NUM_CUS * 8)
+            chunk = min(2048, max(256, _cdiv(chunk, 128) * 128))
+        elif len(blocks) < 2 * NUM_CUS:
+            tiles = sum(_cdiv(b[4], BLOCK_KEYS) for b in blocks)
+            chunk = max(8, _cdiv(tiles, 4 * NUM_CUS)) * BLOCK_KEYS
+    units, merge, partial, any_split = [], [], 0, False
+    for (r, hk, r0, r1, hi) in blocks:
+        n = _cdiv(hi, chunk) if (chunk and hi > chunk) else 1
+        nrows = r1 - r0
+        base = -1
+        if n > 1:
+            any_split = True
+            base = partial
+            partial += n * nrows
+            merge.append([r, hk, r0, r1, base, n, 0, 0])
+        for s_ in range(n):
+            lo = s_ * chunk if n > 1 else 0
+            up = min(hi, lo + chunk) if n > 1 else hi
+            units.append(([r, hk, r0, r1, lo, up, base + s_ * nrows if n > 1 else -1, 0],
+                          (up - lo) * nrows + 1, len(units)))
+    key = lambda u: (-u[1], u[2])
+    if decode or len(units) <= NUM_XCDS:
+        units.sort(key=key)
+        order = [u[0] for u in units]
+    else:
+        grps, i = [], 0
+        while i < len(units):
+            j = i
+            while j < len(units) and units[j][0][:2] == units[i][0][:2]:
+                j += 1
+            grps.append((sum(u[1] for u in units[i:j]), i, j))
+            i = j
+        gorder = sorted(range(len(grps)), key=lambda g: (-grps[g][0], g))
+        queues, load = [[] for _ in range(NUM_XCDS)], [0] * NUM_XCDS
+        for g in gorder:
+            x = min(range(NUM_XCDS), key=lambda k: (load[k], k))
+            load[x] += grps[g][0]
+            queues[x] += [u[0] for u in sorted(units[grps[g][1]:grps[g][2]], key=key)]
+        L = max(len(q) for q in queues)
+        empty = [0, 0, 0, 0, 0, 0, -1, 0]
+        order = [queues[x][i] if i < len(queues[x]) else empty for i in range(L) for x in range(NUM_XCDS)]
+    align = lambda w: _cdiv(w, 64) * 64
+    nnz = 0 if ragged else kv_indptr[B]
+    off_units = 64
+    off_req = off_units + align(len(order) * UNIT_WORDS)
+    off_merge = off_req + align(B * REQ_WORDS)
+    off_idx = off_merge + align(len(merge) * MERGE_WORDS)
+    total = off_idx + align(max(nnz, 1))
+    img = [0] * total
+    hdr = [0x31414b50, 1 if decode else 0, len(order), len(merge), B, nnz, off_units, off_req,
+           off_merge, off_idx, partial, rows_per, chunk if any_split else 0, flags]
+    img[:len(hdr)] = hdr
+    for i, u in enumerate(order):
+        img[off_units + 8 * i: off_units + 8 * i + 8] = u
+    dense = 0
+    for r in range(B):
+        img[off_req + 8 * r: off_req + 8 * r + 5] = [qo_indptr[r], qo_len[r], kv_indptr[r], kv_len[r], dense]
+        dense += kv_len[r]
+    for g, m in enumerate(merge):
+        img[off_merge + 8 * g: off_merge + 8 * g + 8] = m
+    if nnz:
+        img[off_idx: off_idx + nnz] = list(kv_indices)
+    return img
+
+
+def _image(w, flags=0, causal=None):
+    causal = w.causal if causal is None else causal
+    return pka.plan_host_image(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.num_qo_heads,
+                               w.num_kv_heads, w.head_dim, w.page_size, causal, w.num_pages, flags)
+
+
+def _unpack(img):
+    h = img[:16].tolist()
+    n_units, n_merge, B = h[2], h[3], h[4]
+    units = img[h[6]: h[6] + 8 * n_units].view(-1, 8).tolist() if n_units else []
+    req = img[h[7]: h[7] + 8 * B].view(-1, 8).tolist() if B else []
+    merge = img[h[8]: h[8] + 8 * n_merge].view(-1, 8).tolist() if n_merge else []
+    idx = img[h[9]: h[9] + h[5]].tolist()
+    return h, units, req, merge, idx
+
+
+def _random_batch(seed):
+    rng = random.Random(seed)
+    B = rng.randint(1, 6)
+    Hkv = rng.choice([1, 2, 4])
+    G = rng.choice([1, 2, 4, 8])
+    ps = rng.choice([1, 2, 3, 4, 16, 64])
+    decode = rng.random() < 0.3
+    qo, kv = [], []
+    for _ in range(B):
+        k = rng.choice([0, rng.randint(1, 40), rng.randint(40, 3000)])
+        q = (1 if rng.random() < 0.9 else 0) if decode else rng.choice([0, rng.randint(1, 70), rng.randint(1, 600)])
+        qo.append(q)
+        kv.append(k)
+    causal = rng.random() < 0.7
+    return W.build("rand", seed, qo, kv, Hkv * G, Hkv, 64, ps, causal=causal, pool_slack=0.3,
+                   poison=False)
+
+
+CASES = [("seed", s) for s in range(40)]
+
+
+@pytest.mark.parametrize("kind,seed", CASES)
+@pytest.mark.parametrize("flags", [0, pka.PKA_DISABLE_SPLIT_KV])
+def test_coverage_and_restatement(kind, seed, flags):
+    w = _random_batch(seed)
+    img, info = _image(w, flags)
+    img2, _ = _image(w, flags)
+    assert torch.equal(img, img2), "planning must be deterministic"
+    want = restate_plan(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
+                        w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size,
+                        w.causal, flags)
+    assert img.tolist() == want
+    h, units, req, merge, idx = _unpack(img)
+    assert idx == w.kv_indices.tolist()
+    G = w.num_qo_heads // w.num_kv_heads
+    covered = {}
+    for u in units:
+        r, hk, r0, r1, lo, hi, prow, _ = u
+        if r1 == r0:
+            assert lo == hi == 0 and prow == -1  # padding unit
+            continue
+        assert 0 <= lo <= hi <= w.kv_lens[r]
+        for p in range(r0, r1):
+            covered.setdefault((r, hk, p), []).append((lo, hi))
+    for r in range(w.batch):
+        qo, kv = w.qo_lens[r], w.kv_lens[r]
+        for hk in range(w.num_kv_heads):
+            for p in range(qo * G):
+                i = p // G
+                vis_hi = kv if not w.causal else max(0, min(kv, i + kv - qo + 1))
+                ranges = sorted(covered.get((r, hk, p), []))
+                assert ranges, (r, hk, p)
+                # disjoint, contiguous from 0, covering every visible key
+                pos = 0
+                for lo, hi in ranges:
+                    assert lo == pos, (r, hk, p, ranges)
+                    pos = hi
+                assert pos >= vis_hi, (r, hk, p, ranges, vis_hi)
+    if flags & pka.PKA_DISABLE_SPLIT_KV:
+        assert h[3] == 0 and all(u[6] == -1 for u in units)
+    # partial rows: each split group's units write disjoint rows in one block
+    seen = set()
+    for g in merge:
+        r, hk, r0, r1, base, n = g[:6]
+        nrows = r1 - r0
+        parts = sorted(u[6] for u in units if u[0] == r and u[1] == hk and u[2] == r0 and u[6] >= 0)
+        assert parts == [base + s * nrows for s in range(n)]
+        rows = set(range(base, base + n * nrows))
+        assert not rows & seen
+        seen |= rows
+    assert info["num_partial_rows"] == len(seen)
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("dense_vs_sparse", dict(batch=3, length=300, heads=4)),
+    ("gqa_append", dict(batch=5, prefix_range=(10, 900), chunk_range=(1, 200))),
+    ("batch_decode", dict(batch=20)),
+    ("p5_shape", {}),
+])
+def test_named_workloads_restatement(name, kw):
+    w = W.make(name, **kw)
+    img, info = _image(w)
+    want = restate_plan(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
+                        w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size,
+                        w.causal, 0)
+    assert img.tolist() == want
+    a, b = pka.workspace_size(w.qo_indptr, w.kv_indptr, w.kv_last_page_len, w.num_qo_heads,
+                              w.num_kv_heads, w.head_dim, w.page_size, w.causal)
+    assert a == info["int_ws_bytes"] and b == info["float_ws_bytes"]
+
+
+def test_ragged_restatement():
+    w = W.dense_vs_sparse(batch=3, length=200, heads=2, head_dim=64)
+    img, info = pka.plan_host_image(w.qo_indptr, w.kv_token_indptr, None, None, 2, 2, 64, 1, True,
+                                    0, pka.PKA_RAGGED_KV)
+    want = restate_plan(w.qo_indptr.tolist(), w.kv_token_indptr.tolist(), [], None, 2, 2, 1, True,
+                        pka.PKA_RAGGED_KV, ragged=True)
+    assert img.tolist() == want
+
+
+def test_visible_pairs_brute():
+    rng = random.Random(3)
+    for _ in range(200):
+        q, k = rng.randint(0, 30), rng.randint(0, 30)
+        for causal in (True, False):
+            brute = sum(1 for i in range(q) for j in range(k) if not causal or j <= i + k - q)
+            assert pka.visible_pairs([q], [k], causal) == brute
+
+
+# ---------------------------------------------------------------------------
+# Error handling
+# ---------------------------------------------------------------------------
+
+def _expect(code, fn):
+    with pytest.raises(pka.PkaError) as e:
+        fn()
+    assert e.value.code == code, str(e.value)
+    assert str(e.value)
+
+
+def test_errors():
+    ok = dict(qo_indptr=[0, 3, 5], kv_indptr=[0, 2, 3], kv_indices=[4, 1, 0], kv_last_page_len=[2, 1],
+              num_qo_heads=4, num_kv_heads=2, head_dim=64, page_size=4, causal=True, num_pages=8)
+
+    def call(**over):
+        a = dict(ok)
+        a.update(over)
+        return pka.plan_host_image(**a)
+
+    call()  # the baseline is valid
+    E_ARG, E_UNS = pka.PKA_ERR_INVALID_ARG, pka.PKA_ERR_UNSUPPORTED
+    _expect(E_ARG, lambda: call(qo_indptr=[0, 3, 2]))            # decreasing
+    _expect(E_ARG, lambda: call(qo_indptr=[1, 3, 5]))            # does not start at 0
+    _expect(E_ARG, lambda: call(kv_indptr=[0, 3, 2]))
+    _expect(E_ARG, lambda: call(kv_indices=[4, 1, 8]))           # page id out of the pool
+    _expect(E_ARG, lambda: call(kv_indices=[4, -1, 0]))
+    _expect(E_ARG, lambda: call(kv_last_page_len=[0, 1]))        # a used page holds >= 1 slot
+    _expect(E_ARG, lambda: call(kv_last_page_len=[5, 1]))        # > page_size
+    _expect(E_ARG, lambda: call(kv_indptr=[0, 2, 2], kv_indices=[4, 1], kv_last_page_len=[2, 3]))  # empty but last != 0
+    _expect(E_UNS, lambda: call(num_qo_heads=3))                  # Hq % Hkv
+    _expect(E_UNS, lambda: call(head_dim=96))
+    _expect(E_UNS, lambda: call(page_size=0))
+    _expect(E_UNS, lambda: call(page_size=129))
+    _expect(E_ARG, lambda: call(num_kv_heads=0))
+    _expect(E_ARG, lambda: call(flags=0x80))
+    # nnz_pages mismatch and null arrays through the raw ABI
+    L = pka.load_library()
+    i32 = lambda xs: (ctypes.c_int32 * len(xs))(*xs)
+    info = pka.PlanInfo()
+    rc = L.pka_plan_host_image(i32([0, 3, 5]), i32([0, 2, 3]), i32([4, 1, 0]), i32([2, 1]), 2, 2, 8, 4, 2, 64,
+                               4, 1, 0, None, 0, ctypes.byref(info))
+    assert rc == E_ARG and b"nnz" in L.pka_last_error()
+    rc = L.pka_plan_host_image(None, i32([0, 2, 3]), i32([4, 1, 0]), i32([2, 1]), 2, 3, 8, 4, 2, 64, 4, 1, 0,
+                               None, 0, ctypes.byref(info))
+    assert rc == E_ARG
+    rc = L.pka_plan_host_image(i32([0, 3, 5]), i32([0, 2, 3]), None, i32([2, 1]), 2, 3, 8, 4, 2, 64, 4, 1, 0,
+                               None, 0, ctypes.byref(info))
+    assert rc == E_ARG
+    # run / merge_states / debug_gather reject a bad plan or sizes without a GPU
+    assert L.pka_run(None, None, None, None, None, None) == E_ARG
+    assert L.pka_run_ragged(None, None, None, None, None, None, None) == E_ARG
+    assert L.pka_debug_gather(None, None, None, None, None) == E_ARG
+    assert L.pka_merge_states(None, None, 4, 0, 1, 64, None, None, 0, None) == E_ARG
+    assert L.pka_merge_states(None, None, 4, 2, 1, 66, None, None, 0, None) == E_ARG
+    assert L.pka_merge_states(None, None, 0, 2, 1, 64, None, None, 0, None) == pka.PKA_OK  # nothing to do
+    L.pka_plan_destroy(None)  # no-op
+
+
+def test_empty_batch_and_edge_lengths():
+    img, info = pka.plan_host_image([0], [0], [], [], 4, 2, 64, 4, True, 1)
+    assert info["num_units"] == 0 and info["total_q"] == 0
+    # kv_len 0 and qo_len 0 requests plan without error
+    w = W.build("edge", 3, [3, 0, 70, 1], [0, 5, 20, 1], 4, 2, 64, 4, causal=True, pool_slack=0.5)
+    _image(w)
