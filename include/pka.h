@@ -75,7 +75,7 @@ enum { PKA_KERNEL_PREFILL = 0, PKA_KERNEL_DECODE = 1 };
 /* Summary of a plan (all counts are exact for the planned batch). */
 typedef struct pka_plan_info {
   int32_t kernel;           /* PKA_KERNEL_PREFILL or PKA_KERNEL_DECODE                    */
-  int32_t num_units;        /* work units = workgroups of the attention launch             */
+  int32_t num_units;        /* work units (decode: one workgroup each)                      */
   int32_t num_merge_groups; /* split (request, kv head, row block) groups merged afterwards */
   int32_t num_partial_rows; /* fp32 partial-state rows held in the float workspace          */
   int32_t block_rows;       /* packed query rows (token x group head) per work unit         */
@@ -86,6 +86,9 @@ typedef struct pka_plan_info {
   int64_t total_kv;         /* sum of kv_len over the batch                                 */
   int64_t int_ws_bytes;     /* bytes of the int workspace image the plan uploads            */
   int64_t float_ws_bytes;   /* bytes of float workspace the runs need                       */
+  int32_t num_workers;      /* workgroups of the attention launch (prefill: persistent,
+                               each takes units from a queue until it is empty)            */
+  int32_t num_queues;       /* prefill unit queues, one per XCD; 0 for decode                */
 } pka_plan_info;
 
 /* Message for the last failed call on this thread ("" if none). */

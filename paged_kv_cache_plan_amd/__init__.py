@@ -44,7 +44,8 @@ class PlanInfo(ctypes.Structure):
                 ("block_rows", ctypes.c_int32), ("kv_chunk", ctypes.c_int32),
                 ("batch", ctypes.c_int32), ("nnz_pages", ctypes.c_int32),
                 ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64),
-                ("int_ws_bytes", ctypes.c_int64), ("float_ws_bytes", ctypes.c_int64)]
+                ("int_ws_bytes", ctypes.c_int64), ("float_ws_bytes", ctypes.c_int64),
+                ("num_workers", ctypes.c_int32), ("num_queues", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}

@@ -51,7 +51,7 @@ struct pka_plan {
   void* int_ws;
   void* float_ws;
   size_t partial_lse_offset;
-  int32_t off_units, off_req, off_merge, off_idx;
+  int32_t off_units, off_req, off_merge, off_idx, off_sched;
   void* staging;  // pinned copy of the image, read by the enqueued copy
 };
 
@@ -93,6 +93,8 @@ void fill_info(const pka::PlanResult& res, int32_t batch, int32_t nnz, pka_plan_
   info->total_kv = res.total_kv;
   info->int_ws_bytes = static_cast<int64_t>(res.image.size() * sizeof(int32_t));
   info->float_ws_bytes = static_cast<int64_t>(res.float_ws_bytes);
+  info->num_workers = res.num_workers;
+  info->num_queues = res.num_queues;
 }
 
 int plan_or_error(const pka::PlanInput& in, pka::PlanResult* res) {
@@ -118,6 +120,8 @@ pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const v
   a.units = iw + p->off_units;
   a.req = iw + p->off_req;
   a.kv_indices = iw + p->off_idx;
+  a.sched = const_cast<int32_t*>(iw) + p->off_sched;
+  a.num_queues = p->info.num_queues;
   const int64_t row = static_cast<int64_t>(p->num_kv_heads) * p->head_dim;
   const bool ragged = p->flags & PKA_RAGGED_KV;
   a.row_stride = static_cast<int32_t>(row);
@@ -146,7 +150,7 @@ int run_common(const pka_plan* p, const void* q, const void* k, const void* v, v
   if (p->info.kernel == PKA_KERNEL_DECODE)
     e = pka::launch_decode(a, p->head_dim, paged, p->info.num_units, stream);
   else
-    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, p->info.num_units, stream);
+    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, p->info.num_workers, stream);
   if (e != hipSuccess) return hip_error("attention launch", e);
   if (p->info.num_merge_groups > 0) {
     pka::MergeArgs m{};
@@ -258,6 +262,7 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     p->off_req = res.image[pka::kHdrOffReq];
     p->off_merge = res.image[pka::kHdrOffMerge];
     p->off_idx = res.image[pka::kHdrOffIndices];
+    p->off_sched = res.image[pka::kHdrOffSched];
     p->staging = nullptr;
     hipError_t e = hipHostMalloc(&p->staging, need, hipHostMallocDefault);
     if (e != hipSuccess) {

@@ -18,6 +18,7 @@ struct AttnArgs {
   const int32_t* units;      // [num_units][8]
   const int32_t* req;        // [batch][8]
   const int32_t* kv_indices; // [nnz] device copy
+  int32_t* sched;            // prefill: [num_queues][64] queue records with their counters
   int64_t page_stride;       // elements per page: 2 * ps * Hkv * D
   int64_t v_offset;          // elements from a K row to its V row: ps * Hkv * D (paged)
   int32_t row_stride;        // elements between consecutive slots / tokens: Hkv * D
@@ -26,6 +27,7 @@ struct AttnArgs {
   int32_t page_size;
   int32_t page_shift;        // log2(page_size) when a power of two, else -1
   int32_t out_fp32;
+  int32_t num_queues;        // prefill: unit queues (worker b serves queue b % num_queues)
   float scale_log2;          // sm_scale * log2(e): logits in base-2 units
 };
 

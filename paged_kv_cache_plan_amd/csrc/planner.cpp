@@ -197,17 +197,21 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
     if (a.cost != b.cost) return a.cost > b.cost;
     return a.seq < b.seq;
   };
-  if (decode || in.num_xcds <= 1 || units.size() <= static_cast<size_t>(in.num_xcds)) {
+  // Queues (prefill): queue_begin[q] .. queue_begin[q + 1] index the unit array.
+  std::vector<int32_t> queue_begin{0};
+  if (decode) {
     // Longest-first order: the hardware hands out workgroups roughly in index
     // order, so big units start first and small ones fill the tail.
     std::stable_sort(units.begin(), units.end(), longest_first);
+  } else if (in.num_xcds <= 1 || units.size() <= static_cast<size_t>(in.num_xcds)) {
+    std::stable_sort(units.begin(), units.end(), longest_first);
+    queue_begin.push_back(static_cast<int32_t>(units.size()));
   } else {
-    // Prefill: the units of one (request, kv head) read the same K/V, so keep
-    // them on one XCD (workgroup b runs on XCD b % num_xcds) and close in
-    // time, for reuse in that XCD's L2.  Groups go to XCDs longest-first onto
-    // the least loaded queue; each queue runs its groups in that order and
-    // each group's units longest-first.  Queues are padded with empty units
-    // (no rows, no keys) to equal length so the b % num_xcds mapping holds.
+    // The units of one (request, kv head) read the same K/V, so keep them in
+    // one queue, served by the workgroups of one XCD (workgroup b runs on XCD
+    // b % num_xcds), for reuse in that XCD's L2.  Groups go longest-first to
+    // the least loaded queue; a queue runs its groups in that order and each
+    // group's units longest-first, so a group's units run side by side.
     struct Grp { int64_t cost; size_t first, count; };
     std::vector<Grp> grps;
     for (size_t i = 0; i < units.size();) {
@@ -237,16 +241,23 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
       std::stable_sort(g.begin(), g.end(), longest_first);
       queue[x].insert(queue[x].end(), g.begin(), g.end());
     }
-    size_t len = 0;
-    for (const auto& q : queue) len = std::max(len, q.size());
-    Unit empty{};
-    empty.f[kUnitPartialRow] = -1;
-    empty.cost = 0;
     std::vector<Unit> out;
-    out.reserve(len * X);
-    for (size_t i = 0; i < len; ++i)
-      for (int x = 0; x < X; ++x) out.push_back(i < queue[x].size() ? queue[x][i] : empty);
+    out.reserve(units.size());
+    for (int x = 0; x < X; ++x) {
+      out.insert(out.end(), queue[x].begin(), queue[x].end());
+      queue_begin.push_back(static_cast<int32_t>(out.size()));
+    }
     units.swap(out);
+  }
+  const int32_t n_queues = static_cast<int32_t>(queue_begin.size()) - 1;
+  int32_t n_workers = static_cast<int32_t>(units.size());
+  int32_t workers_per_queue = 0;
+  if (n_queues > 0) {
+    int64_t longest = 0;
+    for (int q = 0; q < n_queues; ++q) longest = std::max<int64_t>(longest, queue_begin[q + 1] - queue_begin[q]);
+    const int64_t slots = int64_t(std::max(1, in.num_cus)) * prefill_wg_per_cu(in.head_dim);
+    workers_per_queue = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(longest, slots / n_queues)));
+    n_workers = n_queues * workers_per_queue;
   }
 
   // Assemble the image.
@@ -255,7 +266,8 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   const int32_t off_units = align_words(kHdrWords);
   const int32_t off_req = off_units + align_words(int64_t(n_units) * kUnitWords);
   const int32_t off_merge = off_req + align_words(int64_t(B) * kReqWords);
-  const int32_t off_idx = off_merge + align_words(int64_t(n_merge) * kMergeWords);
+  const int32_t off_sched = off_merge + align_words(int64_t(n_merge) * kMergeWords);
+  const int32_t off_idx = off_sched + align_words(int64_t(n_queues) * kSchedWords);
   const int64_t n_idx = ragged ? 0 : nnz;
   const int64_t total_words = off_idx + align_words(std::max<int64_t>(n_idx, 1));
   out->image.assign(static_cast<size_t>(total_words), 0);
@@ -274,6 +286,15 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   im[kHdrBlockRows] = block_rows;
   im[kHdrKvChunk] = any_split ? static_cast<int32_t>(chunk) : 0;
   im[kHdrFlags] = static_cast<int32_t>(in.flags);
+  im[kHdrOffSched] = off_sched;
+  im[kHdrNumQueues] = n_queues;
+  im[kHdrNumWorkers] = n_workers;
+  for (int32_t q = 0; q < n_queues; ++q) {
+    int32_t* rec = im + off_sched + int64_t(q) * kSchedWords;
+    rec[kSchedBegin] = queue_begin[q];
+    rec[kSchedEnd] = queue_begin[q + 1];
+    rec[kSchedWorkers] = workers_per_queue;
+  }
   for (int32_t i = 0; i < n_units; ++i)
     std::memcpy(im + off_units + int64_t(i) * kUnitWords, units[i].f, sizeof(units[i].f));
   int64_t dense = 0;
@@ -296,6 +317,8 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   out->num_partial_rows = static_cast<int32_t>(partial_rows);
   out->block_rows = block_rows;
   out->kv_chunk = any_split ? static_cast<int32_t>(chunk) : 0;
+  out->num_queues = n_queues;
+  out->num_workers = n_workers;
   out->total_q = in.qo_indptr[B];
   out->total_kv = total_kv;
   const size_t o_bytes = static_cast<size_t>(partial_rows) * in.head_dim * sizeof(float);

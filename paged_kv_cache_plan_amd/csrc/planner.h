@@ -35,7 +35,10 @@ enum HeaderField : int {
   kHdrBlockRows,
   kHdrKvChunk,
   kHdrFlags,
-  kHdrWords = 16
+  kHdrOffSched,     // prefill: per-queue scheduling records (see SchedField)
+  kHdrNumQueues,    // prefill: number of unit queues (0 for decode)
+  kHdrNumWorkers,   // workgroups to launch
+  kHdrWords = 32
 };
 constexpr int32_t kMagic = 0x31414b50;  // "PKA1"
 
@@ -75,6 +78,22 @@ enum MergeField : int {
   kMergeWords = 8
 };
 
+// Prefill runs as a persistent launch: kHdrNumWorkers workgroups, worker b
+// serving queue b % kHdrNumQueues.  Queue q owns units [begin, end) of the
+// unit array; a worker takes the next unit with an atomic increment of the
+// queue's counter.  The last worker of a queue to finish sets both counters
+// back to zero, so the next run of the plan starts from a clean state without
+// a clearing launch.  One 64-word record per queue; the two counters sit on
+// their own 128-byte line, apart from the read-only fields.
+enum SchedField : int {
+  kSchedNext = 0,     // counter: units taken from this queue
+  kSchedDone = 1,     // counter: workers that found the queue empty
+  kSchedBegin = 32,
+  kSchedEnd,
+  kSchedWorkers,      // workers serving this queue
+  kSchedWords = 64
+};
+
 enum Kernel : int { kPrefill = 0, kDecode = 1 };
 
 // Tile shapes the kernels are built for.
@@ -109,6 +128,10 @@ struct PlanInput {
   int32_t num_xcds = 8;           // XCDs workgroups are dealt to round-robin (prefill order)
 };
 
+// Resident prefill workgroups per compute unit the persistent launch aims at
+// (register and LDS use of the kernel for this head_dim).
+constexpr int prefill_wg_per_cu(int head_dim) { return head_dim == 64 ? 3 : 2; }
+
 struct PlanResult {
   int32_t kernel = kPrefill;
   int32_t num_units = 0;
@@ -116,6 +139,8 @@ struct PlanResult {
   int32_t num_partial_rows = 0;
   int32_t block_rows = 0;
   int32_t kv_chunk = 0;
+  int32_t num_queues = 0;   // prefill only
+  int32_t num_workers = 0;  // workgroups of the attention launch
   int64_t total_q = 0;
   int64_t total_kv = 0;
   std::vector<int32_t> image;  // the int workspace image

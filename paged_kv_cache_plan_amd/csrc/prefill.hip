@@ -29,6 +29,7 @@
 #include "args.h"
 #include "device.h"
 #include "launch.h"
+#include "planner.h"
 
 namespace pka {
 namespace {
@@ -50,8 +51,15 @@ template <int CPR>
 __device__ __forceinline__ int k_swz(int key) { return key & (CPR - 1); }
 __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
-template <int D, bool PAGED, bool CAUSAL>
+// How K/V rows are found: a dense ragged array, pages whose power-of-two size
+// is at least one loader thread's run of keys (one page id per thread per
+// tile), smaller power-of-two pages (one id per key, shifts and masks), or
+// pages of any other size (one id per key, division).
+enum KvMode : int { kKvRagged = 0, kKvPagedRun = 1, kKvPagedPow2 = 2, kKvPagedAny = 3 };
+
+template <int D, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
+  constexpr bool PAGED = MODE != kKvRagged;
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
   constexpr int KPT = kBN * CPR / kThreads;  // keys per loader thread: 4 (D=128), 2 (D=64)
   constexpr int DS = D / 16;                 // k-steps of the S^T MFMA
@@ -60,11 +68,28 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
 
   __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * D];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kBN];
+  __shared__ int s_unit[2];
 
-  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
+
+  // Persistent: take units from this worker's queue until it runs dry.
+  int32_t* sched = a.sched + (blockIdx.x % a.num_queues) * kSchedWords;
+  const int q_begin = sched[kSchedBegin], q_end = sched[kSchedEnd];
+  for (int it = 0;; ++it) {
+  if (threadIdx.x == 0)
+    s_unit[it & 1] = q_begin + __hip_atomic_fetch_add(sched + kSchedNext, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  // double-buffered: the slot written next time is read by nobody until
+  // every thread has passed the next barrier
+  const int ui = __builtin_amdgcn_readfirstlane(s_unit[it & 1]);
+  if (ui >= q_end) break;
+  const int32_t* unit = a.units + static_cast<int64_t>(ui) * 8;
+  // Opaque per-unit copy of the thread index: lane-dependent addresses are
+  // recomputed for each unit instead of being held in registers across units.
+  int tid = threadIdx.x;
+  asm volatile("" : "+v"(tid));
   const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int32_t* unit = a.units + static_cast<int64_t>(blockIdx.x) * 8;
   const int r = unit[0], hk = unit[1], row_begin = unit[2], row_end = unit[3];
   const int kv_lo = unit[4], kv_hi = unit[5], prow = unit[6];
   const int32_t* rq = a.req + static_cast<int64_t>(r) * 8;
@@ -81,6 +106,8 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
   const int head = hk * G + ((row_ok ? my_row : wrow0) - tok * G);
   const int lim = tok + kv_len - qo_len;  // last visible key (causal)
   const int wave_lim = wrow0 / G + kv_len - qo_len;  // smallest limit in the wave
+  // keys any row of the wave can see end before wave_hi
+  const int wave_hi = CAUSAL ? min(kv_hi, (min(wrow0 + 32, row_end) - 1) / G + kv_len - qo_len + 1) : kv_hi;
 
   bf16x8 qreg[DS];
   {
@@ -93,47 +120,73 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
   const int lc = tid % CPR;        // 16-byte chunk of the row
   const int lj = tid / CPR;        // key group: keys KPT*lj .. KPT*lj + KPT-1
   const int ps = a.page_size, pshift = a.page_shift;
-  const uint16_t* kbase = a.k + hk * D + 8 * lc;
-  const uint16_t* vbase = PAGED ? kbase + a.v_offset : a.v + hk * D + 8 * lc;
+  // Byte offsets: a page's base is one 32x32 -> 64-bit multiply-add.
+  const uint32_t page_bytes = static_cast<uint32_t>(a.page_stride) * 2u;
+  const uint32_t row_bytes = static_cast<uint32_t>(a.row_stride) * 2u;
+  const char* kbase = reinterpret_cast<const char*>(a.k + hk * D + 8 * lc);
+  const char* vbase = PAGED ? kbase + a.v_offset * 2 : reinterpret_cast<const char*>(a.v + hk * D + 8 * lc);
+  const int32_t* idx = a.kv_indices + kv_base;
+  // A power-of-two page_size >= KPT keeps a thread's KPT keys (KPT-aligned,
+  // tiles start 64-aligned) in one page: one page id per thread per tile.
+  constexpr bool one_page = MODE == kKvPagedRun;
+  constexpr int NID = one_page ? 1 : KPT;
 
   u32x4 kreg[KPT], vreg[KPT];
-  int ids_a[KPT], ids_b[KPT];
+  int ids_a[NID], ids_b[NID];
 
+  constexpr bool pow2 = MODE != kKvPagedAny;
+  auto page_of = [&](int key) { return pow2 ? (key >> pshift) : (key / ps); };
+  auto slot_of = [&](int key) { return pow2 ? (key & (ps - 1)) : (key - (key / ps) * ps); };
   auto fetch_ids = [&](int k0, int* ids) {
     if constexpr (PAGED) {
-      const bool full = k0 + kBN <= kv_hi;  // uniform
+      const int key0 = k0 + KPT * lj;
+      if constexpr (one_page) {
+        ids[0] = key0 < kv_hi ? idx[key0 >> pshift] : 0;
+      } else {
+        const bool full = k0 + kBN <= kv_hi;  // uniform
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) {
-        const int key = k0 + KPT * lj + i;
-        const int pg = pshift >= 0 ? (key >> pshift) : (key / ps);
-        int id = 0;
-        if (full || key < kv_hi) id = a.kv_indices[kv_base + pg];
-        ids[i] = id;
+        for (int i = 0; i < KPT; ++i) {
+          int id = 0;
+          if (full || key0 + i < kv_hi) id = idx[page_of(key0 + i)];
+          ids[i < NID ? i : 0] = id;
+        }
       }
     }
   };
-  auto fetch_one = [&](int key, int id, int i) {
-    int64_t off;
+  // byte offset of key's K row, given the page id
+  auto row_off = [&](int key, int pid) -> uint64_t {
     if constexpr (PAGED) {
-      const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
-      off = static_cast<int64_t>(id) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride;
+      return static_cast<uint64_t>(static_cast<uint32_t>(pid)) * page_bytes +
+             static_cast<uint32_t>(slot_of(key)) * row_bytes;
     } else {
-      off = static_cast<int64_t>(kv_base + key) * a.row_stride;
+      return static_cast<uint64_t>(static_cast<uint32_t>(kv_base + key)) * row_bytes;
     }
-    kreg[i] = ld16(kbase + off);
-    vreg[i] = ld16(vbase + off);
+  };
+  auto fetch_one = [&](int key, int pid, int i) {
+    const uint64_t off = row_off(key, pid);
+    kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
+    vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
   };
   auto fetch_data = [&](int k0, const int* ids) {
+    const int key0 = k0 + KPT * lj;
     if (k0 + kBN <= kv_hi) {  // uniform: the whole tile is in range
+      if constexpr (one_page) {
+        const uint64_t off0 = row_off(key0, ids[0]);
 #pragma unroll
-      for (int i = 0; i < KPT; ++i) fetch_one(k0 + KPT * lj + i, ids[i], i);
+        for (int i = 0; i < KPT; ++i) {
+          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off0 + i * row_bytes);
+          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off0 + i * row_bytes);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < KPT; ++i) fetch_one(key0 + i, ids[i < NID ? i : 0], i);
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        const int key = k0 + KPT * lj + i;
         kreg[i] = u32x4{0, 0, 0, 0};
         vreg[i] = u32x4{0, 0, 0, 0};
-        if (key < kv_hi) fetch_one(key, ids[i], i);
+        if (key0 + i < kv_hi) fetch_one(key0 + i, ids[one_page ? 0 : i], i);
       }
     }
   };
@@ -184,7 +237,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
       if (t + 2 < n_tiles) fetch_ids(k0 + 2 * kBN, ids_b);
     }
 
-    if (wave_active) {
+    if (wave_active && k0 < wave_hi) {  // tiles past every row of the wave are skipped
       // S^T = K . Q^T for two 32-key blocks
       f32x16 s[2];
 #pragma unroll
@@ -198,16 +251,16 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
           s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[st], s[kb], 0, 0, 0);
         }
       }
-      // mask: keys past the unit's range, and (causal) keys past the row's limit
+      // mask: keys past the unit's range, and (causal) keys past the row's
+      // limit; thr = last visible key offset in this tile for the lane's row
       const bool need_mask = (k0 + kBN > kv_hi) || (CAUSAL && k0 + kBN - 1 > wave_lim);
       if (need_mask) {
+        const int thr = (CAUSAL ? min(lim, kv_hi - 1) : kv_hi - 1) - k0 - 4 * half;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const int key = k0 + kb * 32 + 8 * (i >> 2) + 4 * half + (i & 3);
-            if (key >= kv_hi || (CAUSAL && key > lim)) s[kb][i] = -INFINITY;
-          }
+          for (int i = 0; i < 16; ++i)
+            if (kb * 32 + 8 * (i >> 2) + (i & 3) > thr) s[kb][i] = -INFINITY;
       }
       // online softmax in base 2
       float mx = -INFINITY;
@@ -256,9 +309,9 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
   }
 
   // ---- epilogue ------------------------------------------------------------
-  if (!wave_active) return;
+  if (wave_active) {
   const float l_tot = xor32_sum(l_run);
-  if (!row_ok) return;
+  if (row_ok) {
   const bool seen = l_tot > 0.f;
   const float inv = seen ? 1.f / l_tot : 0.f;
   const float lse = seen ? m_run + __log2f(l_tot) : -INFINITY;
@@ -301,15 +354,37 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
       }
     if (half == 0) a.part_lse[prow_i] = lse;
   }
+  }  // row_ok
+  }  // wave_active
+  }  // unit loop
+
+  // The last worker of the queue to get here resets its counters for the
+  // next run; acq_rel orders every worker's final take before the reset.
+  if (threadIdx.x == 0) {
+    const int done = __hip_atomic_fetch_add(sched + kSchedDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == sched[kSchedWorkers] - 1) {
+      __hip_atomic_store(sched + kSchedNext, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sched + kSchedDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
-template <int D, bool PAGED>
-hipError_t launch_prefill_d(const AttnArgs& a, bool causal, int grid, hipStream_t stream) {
+template <int D, int MODE>
+hipError_t launch_prefill_m(const AttnArgs& a, bool causal, int grid, hipStream_t stream) {
   if (causal)
-    prefill_kernel<D, PAGED, true><<<grid, kThreads, 0, stream>>>(a);
+    prefill_kernel<D, MODE, true><<<grid, kThreads, 0, stream>>>(a);
   else
-    prefill_kernel<D, PAGED, false><<<grid, kThreads, 0, stream>>>(a);
+    prefill_kernel<D, MODE, false><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_prefill_d(const AttnArgs& a, bool paged, bool causal, int grid, hipStream_t stream) {
+  constexpr int kRun = kBN * (D / 8) / kThreads;  // keys per loader thread
+  if (!paged) return launch_prefill_m<D, kKvRagged>(a, causal, grid, stream);
+  if (a.page_shift >= 0 && a.page_size >= kRun) return launch_prefill_m<D, kKvPagedRun>(a, causal, grid, stream);
+  if (a.page_shift >= 0) return launch_prefill_m<D, kKvPagedPow2>(a, causal, grid, stream);
+  return launch_prefill_m<D, kKvPagedAny>(a, causal, grid, stream);
 }
 
 }  // namespace
@@ -317,11 +392,8 @@ hipError_t launch_prefill_d(const AttnArgs& a, bool causal, int grid, hipStream_
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool paged, bool causal, int grid,
                           hipStream_t stream) {
   if (grid <= 0) return hipSuccess;
-  if (head_dim == 128)
-    return paged ? launch_prefill_d<128, true>(a, causal, grid, stream)
-                 : launch_prefill_d<128, false>(a, causal, grid, stream);
-  return paged ? launch_prefill_d<64, true>(a, causal, grid, stream)
-               : launch_prefill_d<64, false>(a, causal, grid, stream);
+  if (head_dim == 128) return launch_prefill_d<128>(a, paged, causal, grid, stream);
+  return launch_prefill_d<64>(a, paged, causal, grid, stream);
 }
 
 }  // namespace pka

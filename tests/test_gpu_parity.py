@@ -27,12 +27,43 @@ def test_tiny_non_causal():
     compare(o, lse, *oracle_paged(w), "tiny non-causal")
 
 
-@pytest.mark.parametrize("ps", [1, 3, 16, 64, 128])
+@pytest.mark.parametrize("ps", [1, 2, 3, 4, 8, 16, 64, 128])
 def test_page_sizes(ps):
     w = W.gqa_append(seed=30 + ps, batch=3, prefix_range=(40, 400), chunk_range=(5, 150),
                      page_size=ps)
     o, lse, _ = run_paged(w)
     compare(o, lse, *oracle_paged(w), f"ps={ps}")
+
+
+@pytest.mark.parametrize("ps", [1, 2, 3, 16])
+def test_page_sizes_d64(ps):
+    w = W.gqa_append(seed=50 + ps, batch=3, prefix_range=(40, 400), chunk_range=(5, 150),
+                     page_size=ps, head_dim=64)
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), f"D=64 ps={ps}")
+
+
+def test_repeat_runs_of_one_plan():
+    """Prefill workgroups take units from queues whose counters reset at the
+    end of each launch: every run of one plan must redo the whole batch."""
+    w = W.dense_vs_sparse(seed=7, batch=3, length=300, heads=4)
+    dev = cuda()
+    plan = pka.Plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.num_qo_heads,
+                    w.num_kv_heads, w.head_dim, w.page_size, causal=w.causal, sm_scale=w.sm_scale,
+                    num_pages=w.num_pages, device=dev)
+    assert plan.info["num_queues"] > 1
+    q, pool = w.q.to(dev), w.paged_kv.to(dev)
+    outs = []
+    for _ in range(4):
+        o = torch.full((w.total_q, w.num_qo_heads, w.head_dim), float("nan"), dtype=torch.bfloat16, device=dev)
+        lse = torch.full((w.total_q, w.num_qo_heads), float("nan"), dtype=torch.float32, device=dev)
+        plan.run(q, pool, o, lse)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    plan.close()
+    for o, lse in outs[1:]:
+        assert torch.equal(o, outs[0][0]) and torch.equal(lse, outs[0][1])
+    compare(outs[0][0].float(), outs[0][1], *oracle_paged(w), "repeat")
 
 
 def test_dense_vs_vector_sparse_small():

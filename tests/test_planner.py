@@ -44,7 +44,7 @@ def _cdiv(a, b):
     return -(-a // b)
 
 
-def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, flags, ragged=False):
+def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, flags, ragged=False, D=128):
     B = len(qo_indptr) - 1
     G = Hq // Hkv
     qo_len = [qo_indptr[r + 1] - qo_indptr[r] for r in range(B)]
@@ -98,9 +98,12 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             units.append(([r, hk, r0, r1, lo, up, base + s_ * nrows if n > 1 else -1, 0],
                           (up - lo) * nrows + 1, len(units)))
     key = lambda u: (-u[1], u[2])
+    bounds = [0]  # prefill queue q holds units bounds[q] .. bounds[q + 1]
     if decode or len(units) <= NUM_XCDS:
         units.sort(key=key)
         order = [u[0] for u in units]
+        if not decode:
+            bounds.append(len(order))
     else:
         grps, i = [], 0
         while i < len(units):
@@ -115,20 +118,31 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             x = min(range(NUM_XCDS), key=lambda k: (load[k], k))
             load[x] += grps[g][0]
             queues[x] += [u[0] for u in sorted(units[grps[g][1]:grps[g][2]], key=key)]
-        L = max(len(q) for q in queues)
-        empty = [0, 0, 0, 0, 0, 0, -1, 0]
-        order = [queues[x][i] if i < len(queues[x]) else empty for i in range(L) for x in range(NUM_XCDS)]
+        order = []
+        for q in queues:
+            order += q
+            bounds.append(len(order))
+    nq = len(bounds) - 1
+    workers, per_queue = len(order), 0
+    if nq:
+        longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
+        slots = NUM_CUS * (3 if D == 64 else 2)
+        per_queue = max(1, min(longest, slots // nq))
+        workers = nq * per_queue
     align = lambda w: _cdiv(w, 64) * 64
     nnz = 0 if ragged else kv_indptr[B]
     off_units = 64
     off_req = off_units + align(len(order) * UNIT_WORDS)
     off_merge = off_req + align(B * REQ_WORDS)
-    off_idx = off_merge + align(len(merge) * MERGE_WORDS)
+    off_sched = off_merge + align(len(merge) * MERGE_WORDS)
+    off_idx = off_sched + align(nq * 64)
     total = off_idx + align(max(nnz, 1))
     img = [0] * total
     hdr = [0x31414b50, 1 if decode else 0, len(order), len(merge), B, nnz, off_units, off_req,
-           off_merge, off_idx, partial, rows_per, chunk if any_split else 0, flags]
+           off_merge, off_idx, partial, rows_per, chunk if any_split else 0, flags, off_sched, nq, workers]
     img[:len(hdr)] = hdr
+    for q in range(nq):  # counters (words 0, 1) start at zero
+        img[off_sched + 64 * q + 32: off_sched + 64 * q + 35] = [bounds[q], bounds[q + 1], per_queue]
     for i, u in enumerate(order):
         img[off_units + 8 * i: off_units + 8 * i + 8] = u
     dense = 0
@@ -188,7 +202,7 @@ def test_coverage_and_restatement(kind, seed, flags):
     assert torch.equal(img, img2), "planning must be deterministic"
     want = restate_plan(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
                         w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size,
-                        w.causal, flags)
+                        w.causal, flags, D=w.head_dim)
     assert img.tolist() == want
     h, units, req, merge, idx = _unpack(img)
     assert idx == w.kv_indices.tolist()
@@ -196,9 +210,7 @@ def test_coverage_and_restatement(kind, seed, flags):
     covered = {}
     for u in units:
         r, hk, r0, r1, lo, hi, prow, _ = u
-        if r1 == r0:
-            assert lo == hi == 0 and prow == -1  # padding unit
-            continue
+        assert r0 < r1
         assert 0 <= lo <= hi <= w.kv_lens[r]
         for p in range(r0, r1):
             covered.setdefault((r, hk, p), []).append((lo, hi))
@@ -243,7 +255,7 @@ def test_named_workloads_restatement(name, kw):
     img, info = _image(w)
     want = restate_plan(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
                         w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size,
-                        w.causal, 0)
+                        w.causal, 0, D=w.head_dim)
     assert img.tolist() == want
     a, b = pka.workspace_size(w.qo_indptr, w.kv_indptr, w.kv_last_page_len, w.num_qo_heads,
                               w.num_kv_heads, w.head_dim, w.page_size, w.causal)
@@ -255,8 +267,45 @@ def test_ragged_restatement():
     img, info = pka.plan_host_image(w.qo_indptr, w.kv_token_indptr, None, None, 2, 2, 64, 1, True,
                                     0, pka.PKA_RAGGED_KV)
     want = restate_plan(w.qo_indptr.tolist(), w.kv_token_indptr.tolist(), [], None, 2, 2, 1, True,
-                        pka.PKA_RAGGED_KV, ragged=True)
+                        pka.PKA_RAGGED_KV, ragged=True, D=64)
     assert img.tolist() == want
+
+
+@pytest.mark.parametrize("name,kw", [
+    ("tiny", {}),
+    ("dense_vs_sparse", dict(batch=3, length=300, heads=4)),
+    ("gqa_append", dict(batch=5, prefix_range=(10, 900), chunk_range=(1, 200))),
+])
+def test_prefill_queues(name, kw):
+    """Persistent prefill: the queue records partition the unit array, each
+    (request, kv head) sits in one queue, counters start at zero and the
+    launch size is queues x workers per queue."""
+    w = W.make(name, **kw)
+    img, info = _image(w)
+    h = img[:32].tolist()
+    off_sched, nq, workers = h[14], h[15], h[16]
+    assert info["kernel"] == pka.PKA_KERNEL_PREFILL
+    assert info["num_queues"] == nq >= 1 and info["num_workers"] == workers
+    _, units, _, _, _ = _unpack(img)
+    recs = [img[off_sched + 64 * q: off_sched + 64 * (q + 1)].tolist() for q in range(nq)]
+    assert all(r[0] == 0 and r[1] == 0 for r in recs)
+    assert recs[0][32] == 0 and recs[-1][33] == len(units)
+    assert all(recs[q][33] == recs[q + 1][32] for q in range(nq - 1))
+    per = recs[0][34]
+    assert all(r[34] == per for r in recs) and workers == nq * per
+    assert per <= max(r[33] - r[32] for r in recs)
+    assert workers <= NUM_CUS * (3 if w.head_dim == 64 else 2)
+    home = {}
+    for q, r in enumerate(recs):
+        for u in units[r[32]:r[33]]:
+            assert home.setdefault((u[0], u[1]), q) == q
+
+
+def test_decode_has_no_queues():
+    w = W.batch_decode(batch=20)
+    img, info = _image(w)
+    assert info["kernel"] == pka.PKA_KERNEL_DECODE
+    assert info["num_queues"] == 0 and info["num_workers"] == info["num_units"]
 
 
 def test_visible_pairs_brute():
