@@ -210,8 +210,9 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
     // The units of one (request, kv head) read the same K/V, so keep them in
     // one queue, served by the workgroups of one XCD (workgroup b runs on XCD
     // b % num_xcds), for reuse in that XCD's L2.  Groups go longest-first to
-    // the least loaded queue; a queue runs its groups in that order and each
-    // group's units longest-first, so a group's units run side by side.
+    // the least loaded queue; a queue runs its groups in that order, taking
+    // them in windows of kQueueWindow groups whose units run longest-first,
+    // so a group's units run side by side and long units start early.
     struct Grp { int64_t cost; size_t first, count; };
     std::vector<Grp> grps;
     for (size_t i = 0; i < units.size();) {
@@ -232,14 +233,19 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
     const int X = in.num_xcds;
     std::vector<std::vector<Unit>> queue(X);
     std::vector<int64_t> load(X, 0);
+    std::vector<int32_t> groups_in(X, 0);
+    std::vector<size_t> window_start(X, 0);
     for (size_t gi : order) {
       int x = 0;
       for (int k = 1; k < X; ++k)
         if (load[k] < load[x]) x = k;
       load[x] += grps[gi].cost;
-      std::vector<Unit> g(units.begin() + grps[gi].first, units.begin() + grps[gi].first + grps[gi].count);
-      std::stable_sort(g.begin(), g.end(), longest_first);
-      queue[x].insert(queue[x].end(), g.begin(), g.end());
+      std::vector<Unit>& q = queue[x];
+      if (groups_in[x]++ % kQueueWindow == 0) window_start[x] = q.size();
+      q.insert(q.end(), units.begin() + grps[gi].first, units.begin() + grps[gi].first + grps[gi].count);
+      // stable, by cost only: equal costs keep group order, then planning order
+      std::stable_sort(q.begin() + window_start[x], q.end(),
+                       [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
     }
     std::vector<Unit> out;
     out.reserve(units.size());

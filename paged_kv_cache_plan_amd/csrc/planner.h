@@ -101,6 +101,7 @@ constexpr int kPrefillBlockRows = 128;  // packed query rows per prefill workgro
 constexpr int kPrefillBlockKeys = 64;   // keys per prefill KV tile
 constexpr int kDecodeTileKeys = 32;     // keys per decode wave step
 constexpr int kDecodeMaxGroup = 16;     // decode kernel holds up to 16 query heads per KV head
+constexpr int kQueueWindow = 2;         // prefill queue: groups per longest-first window
 
 constexpr uint32_t kFlagDisableSplit = 0x1u;
 constexpr uint32_t kFlagOutFp32 = 0x2u;

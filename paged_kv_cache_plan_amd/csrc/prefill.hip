@@ -37,6 +37,9 @@ namespace {
 constexpr int kBM = 128;  // packed query rows per workgroup (4 waves x 32)
 constexpr int kBN = 64;   // keys per tile
 constexpr int kThreads = 256;
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008;
+constexpr int kSchedDsRead = 0x100;
 
 // Position of key k (0..63) of a tile inside a V^T row.  Within each group of
 // 16 keys the order is 0-3, 8-11, 4-7, 12-15: exactly the key order in which
@@ -44,11 +47,13 @@ constexpr int kThreads = 256;
 __device__ __forceinline__ int vt_pos(int k) {
   return (k & ~15) + 8 * ((k >> 2) & 1) + 4 * ((k >> 3) & 1) + (k & 3);
 }
-// 16-byte chunk swizzles (XOR), chosen so that the MFMA operand reads are
-// bank-conflict free for 16 lanes per LDS cycle: K rows by key (all chunks
-// of a row), V^T rows by d.
-template <int CPR>
-__device__ __forceinline__ int k_swz(int key) { return key & (CPR - 1); }
+// LDS layouts, chosen so that the MFMA operand reads are bank-conflict free
+// for 16 lanes per LDS cycle.  K rows are padded by one 16-byte chunk (row
+// stride D + 8 elements): 16 consecutive keys then start in 16 different
+// chunk slots, and a lane's eight K reads differ only by immediate offsets.
+// V^T rows (by d) use an XOR swizzle of their 16-byte chunks.
+template <int D>
+constexpr int k_stride() { return D + 8; }
 __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 
 // How K/V rows are found: a dense ragged array, pages whose power-of-two size
@@ -56,6 +61,30 @@ __device__ __forceinline__ int vt_swz(int d) { return (d ^ (d >> 3)) & 7; }
 // tile), smaller power-of-two pages (one id per key, shifts and masks), or
 // pages of any other size (one id per key, division).
 enum KvMode : int { kKvRagged = 0, kKvPagedRun = 1, kKvPagedPow2 = 2, kKvPagedAny = 3 };
+
+// What the kernel reads about one work unit; every field is wave-uniform.
+struct UnitInfo {
+  int r, hk, row_begin, row_end, kv_lo, kv_hi, prow;
+  int qo_begin, qo_len, kv_base, kv_len;
+};
+
+__device__ __forceinline__ UnitInfo load_unit(const AttnArgs& a, int ui) {
+  const int32_t* u = a.units + static_cast<int64_t>(ui) * 8;
+  UnitInfo x;
+  x.r = u[0];
+  x.hk = u[1];
+  x.row_begin = u[2];
+  x.row_end = u[3];
+  x.kv_lo = u[4];
+  x.kv_hi = u[5];
+  x.prow = u[6];
+  const int32_t* rq = a.req + static_cast<int64_t>(x.r) * 8;
+  x.qo_begin = rq[0];
+  x.qo_len = rq[1];
+  x.kv_base = rq[2];
+  x.kv_len = rq[3];
+  return x;
+}
 
 template <int D, int MODE, bool CAUSAL>
 __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
@@ -66,112 +95,97 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
   constexpr int DB = D / 32;                 // 32-row d blocks of O^T
   static_assert(KPT == 2 || KPT == 4, "tile shape");
 
-  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * D];
+  constexpr int KS = k_stride<D>();
+  __shared__ __attribute__((aligned(16))) uint16_t Ks[kBN * KS];
   __shared__ __attribute__((aligned(16))) uint16_t Vt[D * kBN];
   __shared__ int s_unit[2];
 
-  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform
-
-  // Persistent: take units from this worker's queue until it runs dry.
-  int32_t* sched = a.sched + (blockIdx.x % a.num_queues) * kSchedWords;
-  const int q_begin = sched[kSchedBegin], q_end = sched[kSchedEnd];
-  for (int it = 0;; ++it) {
-  if (threadIdx.x == 0)
-    s_unit[it & 1] = q_begin + __hip_atomic_fetch_add(sched + kSchedNext, 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  // double-buffered: the slot written next time is read by nobody until
-  // every thread has passed the next barrier
-  const int ui = __builtin_amdgcn_readfirstlane(s_unit[it & 1]);
-  if (ui >= q_end) break;
-  const int32_t* unit = a.units + static_cast<int64_t>(ui) * 8;
-  // Opaque per-unit copy of the thread index: lane-dependent addresses are
-  // recomputed for each unit instead of being held in registers across units.
-  int tid = threadIdx.x;
-  asm volatile("" : "+v"(tid));
+  const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int r = unit[0], hk = unit[1], row_begin = unit[2], row_end = unit[3];
-  const int kv_lo = unit[4], kv_hi = unit[5], prow = unit[6];
-  const int32_t* rq = a.req + static_cast<int64_t>(r) * 8;
-  const int qo_begin = rq[0], qo_len = rq[1], kv_base = rq[2], kv_len = rq[3];
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
+  const int qcol = lane & 31, half = lane >> 5;  // this lane's query row (MFMA column) and half
+  const int lc = tid % CPR;                      // loader: 16-byte chunk of the row
+  const int lj = tid / CPR;                      // loader: keys KPT*lj .. KPT*lj + KPT-1
   const int G = a.group, Hq = a.num_qo_heads;
-
-  // ---- this lane's query row (MFMA column) --------------------------------
-  const int qcol = lane & 31, half = lane >> 5;
-  const int wrow0 = row_begin + wave * 32;
-  const bool wave_active = wrow0 < row_end;
-  const int my_row = wrow0 + qcol;
-  const bool row_ok = my_row < row_end;
-  const int tok = (row_ok ? my_row : wrow0) / G;
-  const int head = hk * G + ((row_ok ? my_row : wrow0) - tok * G);
-  const int lim = tok + kv_len - qo_len;  // last visible key (causal)
-  const int wave_lim = wrow0 / G + kv_len - qo_len;  // smallest limit in the wave
-  // keys any row of the wave can see end before wave_hi
-  const int wave_hi = CAUSAL ? min(kv_hi, (min(wrow0 + 32, row_end) - 1) / G + kv_len - qo_len + 1) : kv_hi;
-
-  bf16x8 qreg[DS];
-  {
-    const uint16_t* qp = a.q + (static_cast<int64_t>(qo_begin + tok) * Hq + head) * D + 8 * half;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(row_ok ? ld16(qp + 16 * s) : u32x4{0, 0, 0, 0});
-  }
-
-  // ---- loader mapping -------------------------------------------------------
-  const int lc = tid % CPR;        // 16-byte chunk of the row
-  const int lj = tid / CPR;        // key group: keys KPT*lj .. KPT*lj + KPT-1
   const int ps = a.page_size, pshift = a.page_shift;
   // Byte offsets: a page's base is one 32x32 -> 64-bit multiply-add.
   const uint32_t page_bytes = static_cast<uint32_t>(a.page_stride) * 2u;
   const uint32_t row_bytes = static_cast<uint32_t>(a.row_stride) * 2u;
-  const char* kbase = reinterpret_cast<const char*>(a.k + hk * D + 8 * lc);
-  const char* vbase = PAGED ? kbase + a.v_offset * 2 : reinterpret_cast<const char*>(a.v + hk * D + 8 * lc);
-  const int32_t* idx = a.kv_indices + kv_base;
   // A power-of-two page_size >= KPT keeps a thread's KPT keys (KPT-aligned,
   // tiles start 64-aligned) in one page: one page id per thread per tile.
   constexpr bool one_page = MODE == kKvPagedRun;
   constexpr int NID = one_page ? 1 : KPT;
+  constexpr bool pow2 = MODE != kKvPagedAny;
 
+  // Persistent: take units from this worker's queue until it runs dry.  The
+  // next unit is claimed during the current unit's last tile, and its Q and
+  // first K/V tile are in flight while the current unit writes its output.
+  int32_t* sched = a.sched + (blockIdx.x % a.num_queues) * kSchedWords;
+  const int q_begin = sched[kSchedBegin], q_end = sched[kSchedEnd];
+  auto claim = [&](int slot) {
+    if (tid == 0)
+      s_unit[slot] = q_begin + __hip_atomic_fetch_add(sched + kSchedNext, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+  };
+
+  // ---- per-unit lane facts -----------------------------------------------
+  struct Lane {
+    int my_row, tok, head, lim;
+    bool row_ok;
+  };
+  auto lane_of = [&](const UnitInfo& U) {
+    Lane L;
+    const int wrow0 = U.row_begin + wave * 32;
+    L.my_row = wrow0 + qcol;
+    L.row_ok = L.my_row < U.row_end;
+    const int row = L.row_ok ? L.my_row : wrow0;
+    L.tok = row / G;
+    L.head = U.hk * G + (row - L.tok * G);
+    L.lim = L.tok + U.kv_len - U.qo_len;  // last visible key (causal)
+    return L;
+  };
+
+  // ---- loader ----------------------------------------------------------------
   u32x4 kreg[KPT], vreg[KPT];
   int ids_a[NID], ids_b[NID];
+  bf16x8 qreg[DS];
 
-  constexpr bool pow2 = MODE != kKvPagedAny;
   auto page_of = [&](int key) { return pow2 ? (key >> pshift) : (key / ps); };
   auto slot_of = [&](int key) { return pow2 ? (key & (ps - 1)) : (key - (key / ps) * ps); };
-  auto fetch_ids = [&](int k0, int* ids) {
+  auto fetch_ids = [&](const UnitInfo& U, int k0, int* ids) {
     if constexpr (PAGED) {
+      const int32_t* idx = a.kv_indices + U.kv_base;
       const int key0 = k0 + KPT * lj;
       if constexpr (one_page) {
-        ids[0] = key0 < kv_hi ? idx[key0 >> pshift] : 0;
+        ids[0] = key0 < U.kv_hi ? idx[key0 >> pshift] : 0;
       } else {
-        const bool full = k0 + kBN <= kv_hi;  // uniform
+        const bool full = k0 + kBN <= U.kv_hi;  // uniform
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
           int id = 0;
-          if (full || key0 + i < kv_hi) id = idx[page_of(key0 + i)];
+          if (full || key0 + i < U.kv_hi) id = idx[page_of(key0 + i)];
           ids[i < NID ? i : 0] = id;
         }
       }
     }
   };
   // byte offset of key's K row, given the page id
-  auto row_off = [&](int key, int pid) -> uint64_t {
+  auto row_off = [&](const UnitInfo& U, int key, int pid) -> uint64_t {
     if constexpr (PAGED) {
       return static_cast<uint64_t>(static_cast<uint32_t>(pid)) * page_bytes +
              static_cast<uint32_t>(slot_of(key)) * row_bytes;
     } else {
-      return static_cast<uint64_t>(static_cast<uint32_t>(kv_base + key)) * row_bytes;
+      return static_cast<uint64_t>(static_cast<uint32_t>(U.kv_base + key)) * row_bytes;
     }
   };
-  auto fetch_one = [&](int key, int pid, int i) {
-    const uint64_t off = row_off(key, pid);
-    kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
-    vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
-  };
-  auto fetch_data = [&](int k0, const int* ids) {
+  auto fetch_data = [&](const UnitInfo& U, int k0, const int* ids) {
+    const char* kbase = reinterpret_cast<const char*>(a.k + U.hk * D + 8 * lc);
+    const char* vbase =
+        PAGED ? kbase + a.v_offset * 2 : reinterpret_cast<const char*>(a.v + U.hk * D + 8 * lc);
     const int key0 = k0 + KPT * lj;
-    if (k0 + kBN <= kv_hi) {  // uniform: the whole tile is in range
+    if (k0 + kBN <= U.kv_hi) {  // uniform: the whole tile is in range
       if constexpr (one_page) {
-        const uint64_t off0 = row_off(key0, ids[0]);
+        const uint64_t off0 = row_off(U, key0, ids[0]);
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
           kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off0 + i * row_bytes);
@@ -179,14 +193,22 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
         }
       } else {
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) fetch_one(key0 + i, ids[i < NID ? i : 0], i);
+        for (int i = 0; i < KPT; ++i) {
+          const uint64_t off = row_off(U, key0 + i, ids[i < NID ? i : 0]);
+          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
+          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
+        }
       }
     } else {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
         kreg[i] = u32x4{0, 0, 0, 0};
         vreg[i] = u32x4{0, 0, 0, 0};
-        if (key0 + i < kv_hi) fetch_one(key0 + i, ids[one_page ? 0 : i], i);
+        if (key0 + i < U.kv_hi) {
+          const uint64_t off = row_off(U, key0 + i, ids[one_page ? 0 : i]);
+          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
+          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
+        }
       }
     }
   };
@@ -194,7 +216,7 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int key = KPT * lj + i;
-      st16(Ks + key * D + ((lc ^ k_swz<CPR>(key)) * 8), kreg[i]);
+      st16(Ks + key * KS + lc * 8, kreg[i]);
     }
     const int p0 = vt_pos(KPT * lj);
 #pragma unroll
@@ -213,154 +235,214 @@ __global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
       }
     }
   };
-
-  // ---- running state ---------------------------------------------------------
-  f32x16 o[DB];
+  // Q rows of the unit into the MFMA B operand, and its first K/V tile
+  auto start_unit = [&](const UnitInfo& U) {
+    const Lane L = lane_of(U);
+    const uint16_t* qp = a.q + (static_cast<int64_t>(U.qo_begin + L.tok) * Hq + L.head) * D + 8 * half;
 #pragma unroll
-  for (int b = 0; b < DB; ++b) o[b] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
-  const float sl2 = a.scale_log2;
+    for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(L.row_ok ? ld16(qp + 16 * s) : u32x4{0, 0, 0, 0});
+    if (U.kv_hi > U.kv_lo) {
+      fetch_ids(U, U.kv_lo, ids_a);
+      fetch_data(U, U.kv_lo, ids_a);
+      if (U.kv_lo + kBN < U.kv_hi) fetch_ids(U, U.kv_lo + kBN, ids_b);
+    }
+  };
 
-  const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kBN - 1) / kBN : 0;
-  if (n_tiles > 0) {
-    fetch_ids(kv_lo, ids_a);
-    fetch_data(kv_lo, ids_a);
-    if (n_tiles > 1) fetch_ids(kv_lo + kBN, ids_b);
+  claim(0);
+  __syncthreads();
+  int ui = __builtin_amdgcn_readfirstlane(s_unit[0]);
+  int slot = 0;
+  UnitInfo U{};
+  if (ui < q_end) {
+    U = load_unit(a, ui);
+    start_unit(U);
   }
 
-  for (int t = 0; t < n_tiles; ++t) {
-    const int k0 = kv_lo + t * kBN;
-    store_tile();
-    __syncthreads();
-    if (t + 1 < n_tiles) {
-      fetch_data(k0 + kBN, ids_b);
-      if (t + 2 < n_tiles) fetch_ids(k0 + 2 * kBN, ids_b);
-    }
+  while (ui < q_end) {
+    const int lim = lane_of(U).lim;
+    const int wrow0 = U.row_begin + wave * 32;
+    const bool wave_active = wrow0 < U.row_end;
+    const int wave_lim = wrow0 / G + U.kv_len - U.qo_len;  // smallest limit in the wave
+    // keys any row of the wave can see end before wave_hi
+    const int wave_hi =
+        CAUSAL ? min(U.kv_hi, (min(wrow0 + 32, U.row_end) - 1) / G + U.kv_len - U.qo_len + 1) : U.kv_hi;
+    const int kv_lo = U.kv_lo, kv_hi = U.kv_hi;
 
-    if (wave_active && k0 < wave_hi) {  // tiles past every row of the wave are skipped
-      // S^T = K . Q^T for two 32-key blocks
-      f32x16 s[2];
+    f32x16 o[DB];
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        s[kb] = f32x16{};
-        const int key = kb * 32 + qcol;
+    for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+    float m_run = -INFINITY, l_run = 0.f;
+    const float sl2 = a.scale_log2;
+
+    const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kBN - 1) / kBN : 0;
+    if (n_tiles == 0) {
+      claim(slot ^ 1);
+      __syncthreads();
+    }
+    for (int t = 0; t < n_tiles; ++t) {
+      const int k0 = kv_lo + t * kBN;
+      store_tile();
+      __syncthreads();
+      if (t + 1 < n_tiles) {
+        fetch_data(U, k0 + kBN, ids_b);
+        if (t + 2 < n_tiles) fetch_ids(U, k0 + 2 * kBN, ids_b);
+      } else {
+        claim(slot ^ 1);  // visible to all after this tile's closing barrier
+      }
+
+      if (wave_active && k0 < wave_hi) {  // tiles past every row of the wave are skipped
+        // S^T = K . Q^T for two 32-key blocks.  The two blocks' accumulation
+        // chains alternate so that consecutive MFMAs are independent, and the
+        // K operands of step st + 1 are read while step st multiplies.
+        f32x16 s[2] = {f32x16{}, f32x16{}};
+        const uint16_t* kp = Ks + qcol * KS + half * 8;
+        bf16x8 ka[2][2];
+        ka[0][0] = as_bf16x8(ld16(kp));
+        ka[0][1] = as_bf16x8(ld16(kp + 32 * KS));
 #pragma unroll
         for (int st = 0; st < DS; ++st) {
-          const int ch = 2 * st + half;
-          const bf16x8 ka = as_bf16x8(ld16(Ks + key * D + ((ch ^ k_swz<CPR>(key)) * 8)));
-          s[kb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka, qreg[st], s[kb], 0, 0, 0);
+          if (st + 1 < DS) {
+            ka[(st + 1) & 1][0] = as_bf16x8(ld16(kp + (st + 1) * 16));
+            ka[(st + 1) & 1][1] = as_bf16x8(ld16(kp + 32 * KS + (st + 1) * 16));
+          }
+          s[0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1][0], qreg[st], s[0], 0, 0, 0);
+          s[1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(ka[st & 1][1], qreg[st], s[1], 0, 0, 0);
         }
-      }
-      // mask: keys past the unit's range, and (causal) keys past the row's
-      // limit; thr = last visible key offset in this tile for the lane's row
-      const bool need_mask = (k0 + kBN > kv_hi) || (CAUSAL && k0 + kBN - 1 > wave_lim);
-      if (need_mask) {
-        const int thr = (CAUSAL ? min(lim, kv_hi - 1) : kv_hi - 1) - k0 - 4 * half;
+        // issue order: four K reads, then (two MFMAs, two K reads) per step,
+        // so that two steps of operands are in flight
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 4, 0);
+#pragma unroll
+        for (int st = 0; st + 2 < DS; ++st) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 2, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 2, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
+        // mask: keys past the unit's range, and (causal) keys past the row's
+        // limit; thr = last visible key offset in this tile for the lane's row
+        const bool need_mask = (k0 + kBN > kv_hi) || (CAUSAL && k0 + kBN - 1 > wave_lim);
+        if (need_mask) {
+          const int thr = (CAUSAL ? min(lim, kv_hi - 1) : kv_hi - 1) - k0 - 4 * half;
+#pragma unroll
+          for (int kb = 0; kb < 2; ++kb)
+#pragma unroll
+            for (int i = 0; i < 16; ++i)
+              if (kb * 32 + 8 * (i >> 2) + (i & 3) > thr) s[kb][i] = -INFINITY;
+        }
+        // online softmax in base 2
+        float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i)
-            if (kb * 32 + 8 * (i >> 2) + (i & 3) > thr) s[kb][i] = -INFINITY;
-      }
-      // online softmax in base 2
-      float mx = -INFINITY;
+          for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
+        mx = xor32_max(mx);
+        const float m_new = fmaxf(m_run, mx * sl2);
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = fast_exp2(m_run - m_use);
+        float rs = 0.f;
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
+        for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-      mx = xor32_max(mx);
-      const float m_new = fmaxf(m_run, mx * sl2);
-      const float m_use = m_new == -INFINITY ? 0.f : m_new;
-      const float alpha = fast_exp2(m_run - m_use);
-      float rs = 0.f;
+          for (int i = 0; i < 16; ++i) {
+            const float p = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -m_use));
+            s[kb][i] = p;
+            rs += p;
+          }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
+        if (__any(alpha != 1.f)) {  // the running max moved for some row of this wave
 #pragma unroll
-      for (int kb = 0; kb < 2; ++kb)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float p = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -m_use));
-          s[kb][i] = p;
-          rs += p;
+          for (int b = 0; b < DB; ++b) o[b] *= alpha;
         }
-      l_run = l_run * alpha + rs;
-      m_run = m_new;
-      if (__any(alpha != 1.f)) {  // the running max moved for some row of this wave
-#pragma unroll
-        for (int b = 0; b < DB; ++b) o[b] *= alpha;
-      }
 
-      // O^T += V^T . P^T, 16 keys per step
+        // O^T += V^T . P^T, 16 keys per step
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int kb = u >> 1, i0 = 8 * (u & 1);
-        u32x4 pw;
+        for (int u = 0; u < 4; ++u) {
+          const int kb = u >> 1, i0 = 8 * (u & 1);
+          u32x4 pw;
 #pragma unroll
-        for (int w = 0; w < 4; ++w) pw[w] = pack_bf16(s[kb][i0 + 2 * w], s[kb][i0 + 2 * w + 1]);
-        const bf16x8 pb = as_bf16x8(pw);
+          for (int w = 0; w < 4; ++w) pw[w] = pack_bf16(s[kb][i0 + 2 * w], s[kb][i0 + 2 * w + 1]);
+          const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
-        for (int b = 0; b < DB; ++b) {
-          const int d = b * 32 + qcol;
-          const int ch = 2 * u + half;
-          const bf16x8 va = as_bf16x8(ld16(Vt + d * kBN + ((ch ^ vt_swz(d)) * 8)));
-          o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[b], 0, 0, 0);
+          for (int b = 0; b < DB; ++b) {
+            const int d = b * 32 + qcol;
+            const int ch = 2 * u + half;
+            const bf16x8 va = as_bf16x8(ld16(Vt + d * kBN + ((ch ^ vt_swz(d)) * 8)));
+            o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[b], 0, 0, 0);
+          }
+        }
+      }
+      __syncthreads();
+    }
+
+    // ---- next unit: start its loads, then finish this one -------------------
+    // Both s_unit slots alternate: the slot claimed here was last read one
+    // unit ago, before barriers every thread has since passed.
+    const int un = __builtin_amdgcn_readfirstlane(s_unit[slot ^ 1]);
+    const UnitInfo Uc = U;
+    if (un < q_end) {
+      U = load_unit(a, un);
+      start_unit(U);
+    }
+    ui = un;
+    slot ^= 1;
+
+    // ---- epilogue of unit Uc --------------------------------------------------
+    if (wave_active) {
+      const Lane L = lane_of(Uc);
+      // opaque copy: output addresses are formed here, not kept across units
+      int hf = half;
+      asm volatile("" : "+v"(hf));
+      const float l_tot = xor32_sum(l_run);
+      if (L.row_ok) {
+        const bool seen = l_tot > 0.f;
+        const float inv = seen ? 1.f / l_tot : 0.f;
+        const float lse = seen ? m_run + __log2f(l_tot) : -INFINITY;
+        if (Uc.prow < 0) {
+          const int64_t orow = static_cast<int64_t>(Uc.qo_begin + L.tok) * Hq + L.head;
+          if (a.out_fp32) {
+            float* op = static_cast<float*>(a.o) + orow * D;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int d0 = b * 32 + 8 * g + 4 * hf;
+                *reinterpret_cast<f32x4*>(op + d0) =
+                    f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
+              }
+          } else {
+            uint16_t* op = static_cast<uint16_t*>(a.o) + orow * D;
+#pragma unroll
+            for (int b = 0; b < DB; ++b)
+#pragma unroll
+              for (int g = 0; g < 4; ++g) {
+                const int d0 = b * 32 + 8 * g + 4 * hf;
+                u32x2 pk;
+                pk[0] = pack_bf16(o[b][4 * g] * inv, o[b][4 * g + 1] * inv);
+                pk[1] = pack_bf16(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
+                *reinterpret_cast<u32x2*>(op + d0) = pk;
+              }
+          }
+          if (a.lse && hf == 0) a.lse[orow] = lse;
+        } else {
+          const int64_t prow_i = Uc.prow + (L.my_row - Uc.row_begin);
+          float* op = a.part_o + prow_i * D;
+#pragma unroll
+          for (int b = 0; b < DB; ++b)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+              const int d0 = b * 32 + 8 * g + 4 * hf;
+              *reinterpret_cast<f32x4*>(op + d0) =
+                  f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
+            }
+          if (hf == 0) a.part_lse[prow_i] = lse;
         }
       }
     }
-    __syncthreads();
   }
-
-  // ---- epilogue ------------------------------------------------------------
-  if (wave_active) {
-  const float l_tot = xor32_sum(l_run);
-  if (row_ok) {
-  const bool seen = l_tot > 0.f;
-  const float inv = seen ? 1.f / l_tot : 0.f;
-  const float lse = seen ? m_run + __log2f(l_tot) : -INFINITY;
-  if (prow < 0) {
-    const int64_t orow = static_cast<int64_t>(qo_begin + tok) * Hq + head;
-    if (a.out_fp32) {
-      float* op = static_cast<float*>(a.o) + orow * D;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = b * 32 + 8 * g + 4 * half;
-          *reinterpret_cast<f32x4*>(op + d0) =
-              f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
-        }
-    } else {
-      uint16_t* op = static_cast<uint16_t*>(a.o) + orow * D;
-#pragma unroll
-      for (int b = 0; b < DB; ++b)
-#pragma unroll
-        for (int g = 0; g < 4; ++g) {
-          const int d0 = b * 32 + 8 * g + 4 * half;
-          u32x2 pk;
-          pk[0] = pack_bf16(o[b][4 * g] * inv, o[b][4 * g + 1] * inv);
-          pk[1] = pack_bf16(o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv);
-          *reinterpret_cast<u32x2*>(op + d0) = pk;
-        }
-    }
-    if (a.lse && half == 0) a.lse[orow] = lse;
-  } else {
-    const int64_t prow_i = prow + (my_row - row_begin);
-    float* op = a.part_o + prow_i * D;
-#pragma unroll
-    for (int b = 0; b < DB; ++b)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const int d0 = b * 32 + 8 * g + 4 * half;
-        *reinterpret_cast<f32x4*>(op + d0) =
-            f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
-      }
-    if (half == 0) a.part_lse[prow_i] = lse;
-  }
-  }  // row_ok
-  }  // wave_active
-  }  // unit loop
 
   // The last worker of the queue to get here resets its counters for the
   // next run; acq_rel orders every worker's final take before the reset.
-  if (threadIdx.x == 0) {
+  if (tid == 0) {
     const int done = __hip_atomic_fetch_add(sched + kSchedDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
     if (done == sched[kSchedWorkers] - 1) {
       __hip_atomic_store(sched + kSchedNext, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

@@ -23,7 +23,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # Planner constants (paged_kv_cache_plan_amd/csrc/planner.h).
 BLOCK_ROWS, BLOCK_KEYS, DECODE_TILE, DECODE_MAX_G = 128, 64, 32, 16
-NUM_CUS, NUM_XCDS = 256, 8
+NUM_CUS, NUM_XCDS, QUEUE_WINDOW = 256, 8, 2
 UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 8, 8, 8
 
 
@@ -117,7 +117,13 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
         for g in gorder:
             x = min(range(NUM_XCDS), key=lambda k: (load[k], k))
             load[x] += grps[g][0]
-            queues[x] += [u[0] for u in sorted(units[grps[g][1]:grps[g][2]], key=key)]
+            queues[x].append(units[grps[g][1]:grps[g][2]])
+        # windows of QUEUE_WINDOW groups, units longest-first inside a window
+        # (ties: group order, then planning order)
+        queues = [[u[0] for i in range(0, len(gs), QUEUE_WINDOW)
+                   for u in sorted([v for g in gs[i:i + QUEUE_WINDOW] for v in g],
+                                   key=lambda v: -v[1])]
+                  for gs in queues]
         order = []
         for q in queues:
             order += q
