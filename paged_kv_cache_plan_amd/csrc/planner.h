@@ -130,8 +130,9 @@ struct PlanInput {
 };
 
 // Resident prefill workgroups per compute unit the persistent launch aims at
-// (register and LDS use of the kernel for this head_dim).
-constexpr int prefill_wg_per_cu(int head_dim) { return head_dim == 64 ? 3 : 2; }
+// (register and LDS use of the kernel for this head_dim; the kernel is built
+// with the matching launch bound).
+constexpr int prefill_wg_per_cu(int /*head_dim*/) { return 2; }
 
 struct PlanResult {
   int32_t kernel = kPrefill;

@@ -87,7 +87,7 @@ __device__ __forceinline__ UnitInfo load_unit(const AttnArgs& a, int ui) {
 }
 
 template <int D, int MODE, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, 2) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, prefill_wg_per_cu(D)) void prefill_kernel(AttnArgs a) {
   constexpr bool PAGED = MODE != kKvRagged;
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
   constexpr int KPT = kBN * CPR / kThreads;  // keys per loader thread: 4 (D=128), 2 (D=64)

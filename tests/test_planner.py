@@ -132,7 +132,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     workers, per_queue = len(order), 0
     if nq:
         longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
-        slots = NUM_CUS * (3 if D == 64 else 2)
+        slots = NUM_CUS * 2
         per_queue = max(1, min(longest, slots // nq))
         workers = nq * per_queue
     align = lambda w: _cdiv(w, 64) * 64
@@ -300,7 +300,7 @@ def test_prefill_queues(name, kw):
     per = recs[0][34]
     assert all(r[34] == per for r in recs) and workers == nq * per
     assert per <= max(r[33] - r[32] for r in recs)
-    assert workers <= NUM_CUS * (3 if w.head_dim == 64 else 2)
+    assert workers <= NUM_CUS * 2
     home = {}
     for q, r in enumerate(recs):
         for u in units[r[32]:r[33]]:
