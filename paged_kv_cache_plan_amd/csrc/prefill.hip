@@ -37,6 +37,9 @@ namespace {
 constexpr int kBM = 128;  // packed query rows per workgroup (4 waves x 32)
 constexpr int kBN = 64;   // keys per tile
 constexpr int kThreads = 256;
+// Headroom (base-2 units) the running max may lag a row's true max by before
+// O is rescaled (see the online softmax below).
+constexpr float kSlack = 8.f;
 // instruction classes of __builtin_amdgcn_sched_group_barrier
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
@@ -335,9 +338,14 @@ __global__ __launch_bounds__(kThreads, prefill_wg_per_cu(D)) void prefill_kernel
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
         mx = xor32_max(mx);
-        const float m_new = fmaxf(m_run, mx * sl2);
+        // The reference max moves only when this tile's max exceeds it by
+        // more than kSlack (base-2 units): p then stays below 2^kSlack and
+        // the O rescale below is rare after a row's first tile.
+        const float m_tile = mx * sl2;
+        const bool bump = m_tile > m_run + kSlack;
+        const float m_new = bump ? m_tile : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = fast_exp2(m_run - m_use);
+        const float alpha = (bump && m_run != -INFINITY) ? fast_exp2(m_run - m_new) : 1.f;
         float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
