@@ -118,7 +118,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
       for (int hk = 0; hk < Hkv; ++hk) blocks.push_back({r, hk, 0, G, kv_len[r]});
     }
   } else {
-    block_rows = kPrefillBlockRows;
+    block_rows = prefill_block_rows(in.head_dim);
     for (int r = 0; r < B; ++r) {
       if (qo_len[r] == 0) continue;
       const int64_t rows = qo_len[r] * G;

@@ -97,7 +97,6 @@ enum SchedField : int {
 enum Kernel : int { kPrefill = 0, kDecode = 1 };
 
 // Tile shapes the kernels are built for.
-constexpr int kPrefillBlockRows = 128;  // packed query rows per prefill workgroup
 constexpr int kPrefillBlockKeys = 64;   // keys per prefill KV tile
 constexpr int kDecodeTileKeys = 32;     // keys per decode wave step
 constexpr int kDecodeMaxGroup = 16;     // decode kernel holds up to 16 query heads per KV head
@@ -129,10 +128,13 @@ struct PlanInput {
   int32_t num_xcds = 8;           // XCDs workgroups are dealt to round-robin (prefill order)
 };
 
-// Resident prefill workgroups per compute unit the persistent launch aims at
-// (register and LDS use of the kernel for this head_dim; the kernel is built
-// with the matching launch bound).
-constexpr int prefill_wg_per_cu(int /*head_dim*/) { return 2; }
+// Prefill workgroup shape per head_dim: 32 packed query rows per wave, 8
+// waves (256 rows, one resident workgroup per CU) at D=128 and 4 waves (128
+// rows, two per CU) at D=64.  The kernel is built with the matching thread
+// count and launch bound.
+constexpr int prefill_waves(int head_dim) { return head_dim == 128 ? 8 : 4; }
+constexpr int prefill_block_rows(int head_dim) { return 32 * prefill_waves(head_dim); }
+constexpr int prefill_wg_per_cu(int head_dim) { return head_dim == 128 ? 1 : 2; }
 
 struct PlanResult {
   int32_t kernel = kPrefill;

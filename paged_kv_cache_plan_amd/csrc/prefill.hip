@@ -1,9 +1,11 @@
 // Prefill / append attention over a paged (or ragged dense) KV cache, gfx950.
 //
-// One workgroup = one work unit (request r, KV head hk, block of 128 packed
-// query rows, key range [kv_lo, kv_hi)).  Packed row p of a request is token
+// A work unit is (request r, KV head hk, block of packed query rows, key
+// range [kv_lo, kv_hi)); a block is 32 rows per wave, 8 waves (256 rows) at
+// D=128 and 4 waves (128 rows) at D=64.  Packed row p of a request is token
 // p / G and query head hk * G + p % G, so the G query heads that share a KV
-// head share every K/V tile the workgroup loads.
+// head share every K/V tile the workgroup loads.  The launch is persistent:
+// one workgroup per resident slot, each taking units from its XCD's queue.
 //
 // PageAttention is block-sparse attention with page_size-wide blocks
 // (FlashInfer 0.2 release blog, "flexible block sparsity and vector
@@ -16,7 +18,7 @@
 // Per 64-key tile:
 //   loader   each thread fetches KPT keys x one 16-byte chunk of K and V,
 //            issued one tile ahead (page ids two tiles ahead); K goes to LDS
-//            row-major with an XOR swizzle, V is transposed in registers and
+//            row-major in padded rows, V is transposed in registers and
 //            stored as V^T so that the P.V operand is one 16-byte LDS read.
 //   S^T      = K . Q^T with v_mfma_f32_32x32x16_bf16: each wave owns 32 query
 //            rows as MFMA columns, so a lane holds 16 of a row's 32 scores per
@@ -34,9 +36,7 @@
 namespace pka {
 namespace {
 
-constexpr int kBM = 128;  // packed query rows per workgroup (4 waves x 32)
 constexpr int kBN = 64;   // keys per tile
-constexpr int kThreads = 256;
 // Headroom (base-2 units) the running max may lag a row's true max by before
 // O is rescaled (see the online softmax below).
 constexpr float kSlack = 8.f;
@@ -90,10 +90,11 @@ __device__ __forceinline__ UnitInfo load_unit(const AttnArgs& a, int ui) {
 }
 
 template <int D, int MODE, bool CAUSAL>
-__global__ __launch_bounds__(kThreads, prefill_wg_per_cu(D)) void prefill_kernel(AttnArgs a) {
+__global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void prefill_kernel(AttnArgs a) {
+  constexpr int kThreads = 64 * prefill_waves(D);  // 32 packed query rows per wave
   constexpr bool PAGED = MODE != kKvRagged;
   constexpr int CPR = D / 8;                 // 16-byte chunks per K/V row
-  constexpr int KPT = kBN * CPR / kThreads;  // keys per loader thread: 4 (D=128), 2 (D=64)
+  constexpr int KPT = kBN * CPR / kThreads;  // keys per loader thread: 2
   constexpr int DS = D / 16;                 // k-steps of the S^T MFMA
   constexpr int DB = D / 32;                 // 32-row d blocks of O^T
   static_assert(KPT == 2 || KPT == 4, "tile shape");
@@ -462,15 +463,15 @@ __global__ __launch_bounds__(kThreads, prefill_wg_per_cu(D)) void prefill_kernel
 template <int D, int MODE>
 hipError_t launch_prefill_m(const AttnArgs& a, bool causal, int grid, hipStream_t stream) {
   if (causal)
-    prefill_kernel<D, MODE, true><<<grid, kThreads, 0, stream>>>(a);
+    prefill_kernel<D, MODE, true><<<grid, 64 * prefill_waves(D), 0, stream>>>(a);
   else
-    prefill_kernel<D, MODE, false><<<grid, kThreads, 0, stream>>>(a);
+    prefill_kernel<D, MODE, false><<<grid, 64 * prefill_waves(D), 0, stream>>>(a);
   return hipGetLastError();
 }
 
 template <int D>
 hipError_t launch_prefill_d(const AttnArgs& a, bool paged, bool causal, int grid, hipStream_t stream) {
-  constexpr int kRun = kBN * (D / 8) / kThreads;  // keys per loader thread
+  constexpr int kRun = kBN * (D / 8) / (64 * prefill_waves(D));  // keys per loader thread
   if (!paged) return launch_prefill_m<D, kKvRagged>(a, causal, grid, stream);
   if (a.page_shift >= 0 && a.page_size >= kRun) return launch_prefill_m<D, kKvPagedRun>(a, causal, grid, stream);
   if (a.page_shift >= 0) return launch_prefill_m<D, kKvPagedPow2>(a, causal, grid, stream);

@@ -22,7 +22,16 @@ from paged_kv_cache_plan_amd import workloads as W
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
 # Planner constants (paged_kv_cache_plan_amd/csrc/planner.h).
-BLOCK_ROWS, BLOCK_KEYS, DECODE_TILE, DECODE_MAX_G = 128, 64, 32, 16
+BLOCK_KEYS, DECODE_TILE, DECODE_MAX_G = 64, 32, 16
+
+
+def block_rows(D):
+    """Packed query rows per prefill block: 32 per wave, 8 waves at D=128, 4 at D=64."""
+    return 256 if D == 128 else 128
+
+
+def wg_per_cu(D):
+    return 1 if D == 128 else 2
 NUM_CUS, NUM_XCDS, QUEUE_WINDOW = 256, 8, 2
 UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 8, 8, 8
 
@@ -61,14 +70,14 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             if qo_len[r]:
                 blocks += [(r, hk, 0, G, kv_len[r]) for hk in range(Hkv)]
     else:
-        rows_per = BLOCK_ROWS
+        rows_per = block_rows(D)
         for r in range(B):
             if not qo_len[r]:
                 continue
             rows = qo_len[r] * G
             for hk in range(Hkv):
-                for r0 in range(0, rows, BLOCK_ROWS):
-                    r1 = min(rows, r0 + BLOCK_ROWS)
+                for r0 in range(0, rows, rows_per):
+                    r1 = min(rows, r0 + rows_per)
                     hi = kv_len[r]
                     if causal:
                         hi = max(0, min(hi, (r1 - 1) // G + kv_len[r] - qo_len[r] + 1))
@@ -132,7 +141,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     workers, per_queue = len(order), 0
     if nq:
         longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
-        slots = NUM_CUS * 2
+        slots = NUM_CUS * wg_per_cu(D)
         per_queue = max(1, min(longest, slots // nq))
         workers = nq * per_queue
     align = lambda w: _cdiv(w, 64) * 64
@@ -300,7 +309,7 @@ def test_prefill_queues(name, kw):
     per = recs[0][34]
     assert all(r[34] == per for r in recs) and workers == nq * per
     assert per <= max(r[33] - r[32] for r in recs)
-    assert workers <= NUM_CUS * 2
+    assert workers <= NUM_CUS * wg_per_cu(w.head_dim)
     home = {}
     for q, r in enumerate(recs):
         for u in units[r[32]:r[33]]:
