@@ -37,7 +37,7 @@ if ROOT not in sys.path:
 PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "causal paged prefill TFLOP/s (D=128) and decode HBM GB/s, % of roofline"
-KERNEL_SOURCES = ["prefill.hip", "decode.hip", "merge.hip", "device.h", "args.h"]
+KERNEL_SOURCES = ["prefill.hip", "decode.hip", "merge.hip", "device.h", "args.h", "planner.h"]
 
 
 def kernel_source_hash() -> str:
