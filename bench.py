@@ -145,6 +145,39 @@ def bench_workload(name, w, dev, steps, warmup, ragged=False, copies=2):
     return res
 
 
+def bench_append(w, dev, steps, warmup, copies=4, pools=2):
+    """Paged-KV append of one batch: the batch-indices/positions launch and
+    the copy launch, each timed with HIP events on the launch stream.  Four
+    copies of the appended rows and two pools alternate, so the working set
+    (~430 MB) exceeds the 256 MB MALL; every launch rewrites the same slots."""
+    import torch
+    import paged_kv_cache_plan_amd as pka
+    ind, sl = w.append_indptr.to(dev), w.seq_lens.to(dev)
+    kvi, kvp = w.kv_indices.to(dev), w.kv_indptr.to(dev)
+    ks = [w.append_k] + [w.append_k.clone() for _ in range(copies - 1)]
+    vs = [w.append_v] + [w.append_v.clone() for _ in range(copies - 1)]
+    bi, pos = pka.get_batch_indices_positions(ind, sl, w.nnz)
+    pls = [w.paged_kv] + [w.paged_kv.clone() for _ in range(pools - 1)]
+
+    def idx_launch(i):
+        pka.get_batch_indices_positions(ind, sl, w.nnz)
+
+    def app_launch(i):
+        c = i % copies
+        pka.append_paged_kv(ks[c], vs[c], bi, pos, pls[i % pools], kvi, kvp)
+
+    _, per_idx = time_launches(idx_launch, steps, warmup)
+    total_ms, per = time_launches(app_launch, steps, warmup)
+    avg = sum(per) / len(per)
+    row = w.num_kv_heads * w.head_dim * 2
+    b = w.nnz * (4 * row + 8)  # K and V rows read and written, plus the index pair
+    return {"ms_per_step": total_ms / steps, "launch_ms_avg": avg, "launch_ms_min": min(per),
+            "indices_launch_ms_avg": sum(per_idx) / len(per_idx), "tokens": w.nnz,
+            "algorithmic_bytes": b, "GB_per_s": b / (avg * 1e-3) / 1e9,
+            "frac_of_hbm_peak": b / (avg * 1e-3) / 1e9 / PEAK_HBM_GBS, "kernel": "append"}
+    # (the caller drops the workload afterwards; the copies go with this frame)
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The CPU fp64 oracle, as it stands, on a bounded sample of the headline
     workload (the same inputs the GPU was timed on, copied to the host):
@@ -187,7 +220,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
-                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5 (profiling runs)")
+                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5, append (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -247,6 +280,11 @@ def main():
         results["batch_decode"] = bench_workload("c5", w5, dev, args.steps, args.warmup)
         print(f"# c5: {results['batch_decode']}", file=sys.stderr, flush=True)
         del w5
+    if want("append"):
+        wa = W.chunk_append(device=dev)
+        results["chunk_append"] = bench_append(wa, dev, args.steps, args.warmup)
+        print(f"# append: {results['chunk_append']}", file=sys.stderr, flush=True)
+        del wa
     torch.cuda.empty_cache()
 
     if sel is not None:

@@ -180,6 +180,48 @@ int pka_merge_states(const float* v, const float* s, int64_t n, int32_t num_stat
 int pka_debug_gather(const pka_plan* plan, const void* paged_kv, void* k_dense, void* v_dense,
                      pka_stream_t stream);
 
+/*
+ * Request and position of every appended token, for a per-element append
+ * (FlashInfer 0.2 release blog, "KV-cache append optimisation":
+ * get_batch_indices_positions).
+ *   append_indptr [batch+1]: DEVICE int32; request r appends the tokens
+ *     append_indptr[r] .. append_indptr[r+1]-1 of the appended tensors;
+ *   seq_lens [batch]: DEVICE int32, each request's KV length AFTER the
+ *     append; its n_r appended tokens are its last n_r tokens;
+ *   nnz = append_indptr[batch], given by the caller;
+ *   batch_indices, positions [nnz]: DEVICE int32 outputs, token i of
+ *     request r getting r and seq_lens[r] - n_r + (i - append_indptr[r]).
+ * Asynchronous on `stream`.  Null pointers or negative sizes ->
+ * PKA_ERR_INVALID_ARG; the device arrays themselves are not validated.
+ */
+int pka_get_batch_indices_positions(const int32_t* append_indptr, const int32_t* seq_lens,
+                                    int32_t batch, int32_t nnz, int32_t* batch_indices,
+                                    int32_t* positions, pka_stream_t stream);
+
+/*
+ * Write appended K/V rows into the paged cache (FlashInfer documentation,
+ * "flashinfer.page: Append new K/V tensors to Paged KV-Cache").
+ *   append_k, append_v: DEVICE bf16 [nnz, num_kv_heads, head_dim];
+ *   batch_indices, positions: DEVICE int32 [nnz] (see above);
+ *   paged_kv: DEVICE bf16 [num_pages, 2, page_size, num_kv_heads, head_dim]
+ *     (NHD; 0 = K, 1 = V), updated in place;
+ *   kv_indptr [batch+1], kv_indices [kv_indptr[batch]]: DEVICE int32 page
+ *     table already covering the lengths after the append.
+ * Token i goes to page kv_indices[kv_indptr[b] + p / page_size], slot
+ * p % page_size, with b = batch_indices[i], p = positions[i] -- the slot the
+ * attention kernels read position p from.  A token whose b is outside
+ * [0, batch), whose p is negative or past the request's pages, or whose page
+ * id is outside [0, num_pages) is skipped: nothing is written for it.
+ * Tokens that map to the same slot race.  head_dim must be 64 or 128 and
+ * page_size in [1, 128] (PKA_ERR_UNSUPPORTED otherwise); the K/V tensors must
+ * be 16-byte aligned (PKA_ERR_INVALID_ARG).  Asynchronous on `stream`.
+ */
+int pka_append_paged_kv(const void* append_k, const void* append_v, const int32_t* batch_indices,
+                        const int32_t* positions, int32_t nnz, void* paged_kv, int32_t num_pages,
+                        int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
+                        const int32_t* kv_indices, const int32_t* kv_indptr, int32_t batch,
+                        pka_stream_t stream);
+
 /* Free a plan.  The caller must first make sure the plan's copy and every run
  * using it have completed (for example by synchronising the stream).  NULL is
  * a no-op. */

@@ -35,7 +35,8 @@ PKA_KERNEL_DECODE = 1
 
 EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka_plan_get_info",
             "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
-            "pka_debug_gather", "pka_plan_destroy"]
+            "pka_debug_gather", "pka_plan_destroy", "pka_get_batch_indices_positions",
+            "pka_append_paged_kv"]
 
 
 class PlanInfo(ctypes.Structure):
@@ -91,6 +92,10 @@ def load_library(path: str = LIB_PATH):
     L.pka_merge_states.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp, vp, u32, vp]
     L.pka_debug_gather.restype = ctypes.c_int
     L.pka_debug_gather.argtypes = [vp, vp, vp, vp, vp]
+    L.pka_get_batch_indices_positions.restype = ctypes.c_int
+    L.pka_get_batch_indices_positions.argtypes = [vp, vp, i32, i32, vp, vp, vp]
+    L.pka_append_paged_kv.restype = ctypes.c_int
+    L.pka_append_paged_kv.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, vp]
     L.pka_plan_destroy.restype = None
     L.pka_plan_destroy.argtypes = [vp]
     _lib = L
@@ -290,6 +295,49 @@ def merge_states(v, s, out_fp32=True, stream=None):
                               _dev_ptr(v_out, "v_out"), _dev_ptr(s_out, "s_out"),
                               PKA_OUT_FP32 if out_fp32 else 0, _stream_ptr(stream)))
     return v_out, s_out
+
+
+def get_batch_indices_positions(append_indptr, seq_lens, nnz, stream=None):
+    """Request and position of every appended token (device int32 [nnz] each).
+
+    append_indptr int32 [batch+1] and seq_lens int32 [batch] (lengths after
+    the append) are GPU tensors; nnz = append_indptr[batch]."""
+    import torch
+    L = load_library()
+    batch = seq_lens.numel()
+    if append_indptr.numel() != batch + 1:
+        raise ValueError("append_indptr must have batch + 1 entries")
+    bi = torch.empty(nnz, dtype=torch.int32, device=seq_lens.device)
+    pos = torch.empty(nnz, dtype=torch.int32, device=seq_lens.device)
+    _check(L.pka_get_batch_indices_positions(_dev_ptr(append_indptr, "append_indptr", torch.int32),
+                                             _dev_ptr(seq_lens, "seq_lens", torch.int32), batch, nnz,
+                                             _dev_ptr(bi, "batch_indices"), _dev_ptr(pos, "positions"),
+                                             _stream_ptr(stream)))
+    return bi, pos
+
+
+def append_paged_kv(append_k, append_v, batch_indices, positions, paged_kv, kv_indices, kv_indptr,
+                    stream=None):
+    """Write appended K/V rows (bf16 [nnz, Hkv, D]) into paged_kv
+    (bf16 [num_pages, 2, ps, Hkv, D]) in place, through the page table."""
+    import torch
+    L = load_library()
+    nnz, Hkv, D = append_k.shape
+    if tuple(append_v.shape) != (nnz, Hkv, D):
+        raise ValueError("append_v must match append_k")
+    num_pages, two, ps, Hkv2, D2 = paged_kv.shape
+    if two != 2 or Hkv2 != Hkv or D2 != D:
+        raise ValueError("paged_kv must be [num_pages, 2, page_size, Hkv, D] matching the appended rows")
+    if batch_indices.numel() != nnz or positions.numel() != nnz:
+        raise ValueError("batch_indices and positions must have nnz entries")
+    _check(L.pka_append_paged_kv(_dev_ptr(append_k, "append_k", torch.bfloat16),
+                                 _dev_ptr(append_v, "append_v", torch.bfloat16),
+                                 _dev_ptr(batch_indices, "batch_indices", torch.int32),
+                                 _dev_ptr(positions, "positions", torch.int32), nnz,
+                                 _dev_ptr(paged_kv, "paged_kv", torch.bfloat16), num_pages, ps, Hkv, D,
+                                 _dev_ptr(kv_indices, "kv_indices", torch.int32),
+                                 _dev_ptr(kv_indptr, "kv_indptr", torch.int32), kv_indptr.numel() - 1,
+                                 _stream_ptr(stream)))
 
 
 def visible_pairs(qo_lens, kv_lens, causal=True) -> int:

@@ -24,7 +24,7 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpka.so")
 ARCH = "gfx950"
-KERNELS = ["prefill.hip", "decode.hip", "merge.hip"]
+KERNELS = ["prefill.hip", "decode.hip", "merge.hip", "append.hip"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]

@@ -357,6 +357,65 @@ int pka_debug_gather(const pka_plan* plan, const void* paged_kv, void* k_dense, 
   return PKA_OK;
 }
 
+int pka_get_batch_indices_positions(const int32_t* append_indptr, const int32_t* seq_lens, int32_t batch,
+                                    int32_t nnz, int32_t* batch_indices, int32_t* positions,
+                                    pka_stream_t stream) {
+  if (batch < 0 || nnz < 0) return set_error(PKA_ERR_INVALID_ARG, "batch_indices_positions: negative size");
+  if (nnz == 0) return PKA_OK;
+  if (batch == 0) return set_error(PKA_ERR_INVALID_ARG, "batch_indices_positions: nnz > 0 with no request");
+  if (!append_indptr || !seq_lens || !batch_indices || !positions)
+    return set_error(PKA_ERR_INVALID_ARG, "batch_indices_positions: null pointer");
+  pka::BatchPosArgs a{};
+  a.append_indptr = append_indptr;
+  a.seq_lens = seq_lens;
+  a.batch_indices = batch_indices;
+  a.positions = positions;
+  a.batch = batch;
+  a.nnz = nnz;
+  const hipError_t e = pka::launch_batch_indices_positions(a, stream);
+  if (e != hipSuccess) return hip_error("batch_indices_positions launch", e);
+  return PKA_OK;
+}
+
+int pka_append_paged_kv(const void* append_k, const void* append_v, const int32_t* batch_indices,
+                        const int32_t* positions, int32_t nnz, void* paged_kv, int32_t num_pages,
+                        int32_t page_size, int32_t num_kv_heads, int32_t head_dim, const int32_t* kv_indices,
+                        const int32_t* kv_indptr, int32_t batch, pka_stream_t stream) {
+  if (nnz < 0 || batch < 0 || num_pages < 0) return set_error(PKA_ERR_INVALID_ARG, "append: negative size");
+  if (head_dim != 64 && head_dim != 128) return set_error(PKA_ERR_UNSUPPORTED, "append: head_dim must be 64 or 128");
+  if (num_kv_heads < 1) return set_error(PKA_ERR_INVALID_ARG, "append: num_kv_heads must be >= 1");
+  if (page_size < 1 || page_size > 128) return set_error(PKA_ERR_UNSUPPORTED, "append: page_size must be in [1, 128]");
+  const int64_t row = static_cast<int64_t>(num_kv_heads) * head_dim;
+  if (row > (int64_t(1) << 24) || static_cast<int64_t>(num_pages) * 2 * page_size * row > (int64_t(1) << 62))
+    return set_error(PKA_ERR_UNSUPPORTED, "append: sizes too large");
+  if (nnz == 0) return PKA_OK;
+  if (!append_k || !append_v || !batch_indices || !positions || !paged_kv || !kv_indices || !kv_indptr)
+    return set_error(PKA_ERR_INVALID_ARG, "append: null pointer");
+  for (const void* ptr : {append_k, append_v, static_cast<const void*>(paged_kv)})
+    if (reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return set_error(PKA_ERR_INVALID_ARG, "append: K/V tensors must be 16-byte aligned");
+  pka::AppendArgs a{};
+  a.append_k = static_cast<const uint16_t*>(append_k);
+  a.append_v = static_cast<const uint16_t*>(append_v);
+  a.batch_indices = batch_indices;
+  a.positions = positions;
+  a.paged_kv = static_cast<uint16_t*>(paged_kv);
+  a.kv_indices = kv_indices;
+  a.kv_indptr = kv_indptr;
+  a.nnz = nnz;
+  a.batch = batch;
+  a.num_pages = num_pages;
+  a.page_size = page_size;
+  int shift = -1;
+  for (int sh = 0; sh < 8; ++sh)
+    if ((1 << sh) == page_size) shift = sh;
+  a.page_shift = shift;
+  a.row_elems = static_cast<int32_t>(row);
+  const hipError_t e = pka::launch_append(a, stream);
+  if (e != hipSuccess) return hip_error("append launch", e);
+  return PKA_OK;
+}
+
 void pka_plan_destroy(pka_plan* plan) {
   if (!plan_ok(plan)) return;
   if (plan->staging) (void)hipHostFree(plan->staging);

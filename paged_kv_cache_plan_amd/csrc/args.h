@@ -72,4 +72,31 @@ struct GatherArgs {
   int32_t head_dim;
 };
 
+// Arguments of get_batch_indices_positions.
+struct BatchPosArgs {
+  const int32_t* append_indptr;  // [batch + 1]
+  const int32_t* seq_lens;       // [batch], KV lengths after the append
+  int32_t* batch_indices;        // [nnz]
+  int32_t* positions;            // [nnz]
+  int32_t batch;
+  int32_t nnz;
+};
+
+// Arguments of the paged-KV append.  Element offsets count bf16 elements.
+struct AppendArgs {
+  const uint16_t* append_k;      // [nnz, Hkv, D]
+  const uint16_t* append_v;      // [nnz, Hkv, D]
+  const int32_t* batch_indices;  // [nnz]
+  const int32_t* positions;      // [nnz]
+  uint16_t* paged_kv;            // [num_pages, 2, ps, Hkv, D]
+  const int32_t* kv_indices;     // [kv_indptr[batch]]
+  const int32_t* kv_indptr;      // [batch + 1]
+  int32_t nnz;
+  int32_t batch;
+  int32_t num_pages;
+  int32_t page_size;
+  int32_t page_shift;            // log2(page_size) when a power of two, else -1
+  int32_t row_elems;             // Hkv * D
+};
+
 }  // namespace pka

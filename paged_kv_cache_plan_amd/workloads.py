@@ -269,3 +269,80 @@ WORKLOADS = {
 
 def make(name: str, **kw) -> Workload:
     return WORKLOADS[name](**kw)
+
+
+# ---------------------------------------------------------------------------
+# Appending K/V rows to the paged cache.
+# ---------------------------------------------------------------------------
+
+@dataclass
+class AppendWorkload:
+    name: str
+    seed: int
+    batch: int
+    num_kv_heads: int
+    head_dim: int
+    page_size: int
+    prior_lens: list       # KV length of each request before the append
+    append_lens: list      # tokens appended to each request
+    append_indptr: torch.Tensor   # int32 [B+1]
+    seq_lens: torch.Tensor        # int32 [B], lengths after the append
+    kv_indptr: torch.Tensor       # int32 [B+1], page table for seq_lens
+    kv_indices: torch.Tensor
+    kv_last_page_len: torch.Tensor
+    num_pages: int
+    paged_kv: torch.Tensor        # bf16 [num_pages, 2, ps, Hkv, D], the cache before the append
+    append_k: torch.Tensor        # bf16 [nnz, Hkv, D]
+    append_v: torch.Tensor
+
+    @property
+    def nnz(self):
+        return int(self.append_indptr[-1])
+
+
+def build_append(name, seed, prior_lens, append_lens, num_kv_heads, head_dim, page_size,
+                 pool_slack=0.1, gen=None, device="cpu") -> AppendWorkload:
+    """Draw order after the lengths: page permutation -> pool -> appended K -> V."""
+    gen = gen if gen is not None else torch.Generator("cpu").manual_seed(seed)
+    B = len(prior_lens)
+    seq = [a + b for a, b in zip(prior_lens, append_lens)]
+    ps = page_size
+    nnz_pages = sum((L + ps - 1) // ps for L in seq)
+    num_pages = max(1, nnz_pages + int(math.ceil(nnz_pages * pool_slack)))
+    kv_indptr, kv_indices, last = page_table_for(seq, ps, num_pages, gen)
+    app = torch.tensor([0] + list(torch.tensor(append_lens, dtype=torch.int64).cumsum(0).tolist()),
+                       dtype=torch.int32)
+    dev = torch.device(device)
+    vgen = gen if dev.type == "cpu" else torch.Generator(device=dev).manual_seed(seed)
+    pool = _randn_bf16((num_pages, 2, ps, num_kv_heads, head_dim), vgen)
+    nnz = int(app[-1])
+    k = _randn_bf16((nnz, num_kv_heads, head_dim), vgen)
+    v = _randn_bf16((nnz, num_kv_heads, head_dim), vgen)
+    return AppendWorkload(name=name, seed=seed, batch=B, num_kv_heads=num_kv_heads, head_dim=head_dim,
+                          page_size=ps, prior_lens=list(prior_lens), append_lens=list(append_lens),
+                          append_indptr=app, seq_lens=torch.tensor(seq, dtype=torch.int32),
+                          kv_indptr=kv_indptr, kv_indices=kv_indices, kv_last_page_len=last,
+                          num_pages=num_pages, paged_kv=pool, append_k=k, append_v=v)
+
+
+def chunk_append(seed=7, batch=32, prefix_range=(512, 8192), chunk_range=(64, 1024), num_kv_heads=8,
+                 head_dim=128, page_size=16, **kw) -> AppendWorkload:
+    """The append in front of the GQA append-prefill: B=32 requests with a
+    prefix ~U{512..8192} already cached append a chunk ~U{64..1024} of
+    tokens, Hkv=8, D=128, page_size=16, 10% pool slack."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    P = _uniform_int(gen, prefix_range[0], prefix_range[1], batch)
+    n = _uniform_int(gen, chunk_range[0], chunk_range[1], batch)
+    return build_append("chunk_append", seed, P, n, num_kv_heads, head_dim, page_size, gen=gen, **kw)
+
+
+def decode_append(seed=8, batch=256, kv_log2_range=(7.0, 15.0), kv_clamp=(128, 32768), num_kv_heads=8,
+                  head_dim=128, page_size=16, **kw) -> AppendWorkload:
+    """One decode step's append: every request of the batch-decode shape
+    appends one token (lengths log-uniform, clamped)."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    u = torch.rand(batch, generator=gen, dtype=torch.float64)
+    lo, hi = kv_log2_range
+    L = [int(min(kv_clamp[1], max(kv_clamp[0], round(2.0 ** (lo + (hi - lo) * float(x)))))) for x in u]
+    return build_append("decode_append", seed, [x - 1 for x in L], [1] * batch, num_kv_heads, head_dim,
+                        page_size, gen=gen, **kw)
