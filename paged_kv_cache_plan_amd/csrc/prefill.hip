@@ -118,7 +118,10 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
   // A power-of-two page_size >= KPT keeps a thread's KPT keys (KPT-aligned,
   // tiles start 64-aligned) in one page: one page id per thread per tile.
   constexpr bool one_page = MODE == kKvPagedRun;
-  constexpr int NID = one_page ? 1 : KPT;
+  // Single-key pages with KPT == 2: the two lanes of a pair load one page id
+  // each and swap them with one DPP move.
+  constexpr bool pair_ids = MODE == kKvPagedPow2 && KPT == 2;
+  constexpr int NID = (one_page || pair_ids) ? 1 : KPT;
   constexpr bool pow2 = MODE != kKvPagedAny;
 
   // Persistent: take units from this worker's queue until it runs dry.  The
@@ -162,6 +165,9 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
       const int key0 = k0 + KPT * lj;
       if constexpr (one_page) {
         ids[0] = key0 < U.kv_hi ? idx[key0 >> pshift] : 0;
+      } else if constexpr (pair_ids) {
+        const int mine = key0 + (lc & 1);  // page_size 1: page = key
+        ids[0] = mine < U.kv_hi ? idx[mine] : 0;
       } else {
         const bool full = k0 + kBN <= U.kv_hi;  // uniform
 #pragma unroll
@@ -182,7 +188,16 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
       return static_cast<uint64_t>(static_cast<uint32_t>(U.kv_base + key)) * row_bytes;
     }
   };
-  auto fetch_data = [&](const UnitInfo& U, int k0, const int* ids) {
+  auto fetch_data = [&](const UnitInfo& U, int k0, const int* ids_in) {
+    int pair[2];
+    const int* ids = ids_in;
+    if constexpr (pair_ids) {
+      // quad_perm [1, 0, 3, 2]: the partner lane's id (lanes 2m, 2m + 1 share lj)
+      const int other = __builtin_amdgcn_mov_dpp(ids_in[0], 0xB1, 0xF, 0xF, true);
+      pair[0] = (lc & 1) ? other : ids_in[0];
+      pair[1] = (lc & 1) ? ids_in[0] : other;
+      ids = pair;
+    }
     const char* kbase = reinterpret_cast<const char*>(a.k + U.hk * D + 8 * lc);
     const char* vbase =
         PAGED ? kbase + a.v_offset * 2 : reinterpret_cast<const char*>(a.v + U.hk * D + 8 * lc);
@@ -198,7 +213,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
       } else {
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
-          const uint64_t off = row_off(U, key0 + i, ids[i < NID ? i : 0]);
+          const uint64_t off = row_off(U, key0 + i, ids[(i < NID || pair_ids) ? i : 0]);
           kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
           vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
         }
@@ -209,7 +224,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
         kreg[i] = u32x4{0, 0, 0, 0};
         vreg[i] = u32x4{0, 0, 0, 0};
         if (key0 + i < U.kv_hi) {
-          const uint64_t off = row_off(U, key0 + i, ids[one_page ? 0 : i]);
+          const uint64_t off = row_off(U, key0 + i, ids[one_page ? 0 : i]);  // pair_ids: ids = pair
           kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
           vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
         }
