@@ -155,6 +155,25 @@ int pka_plan_host_image(const int32_t* qo_indptr, const int32_t* kv_indptr,
 int pka_run(const pka_plan* plan, const void* q, const void* paged_kv, void* o, float* lse,
             pka_stream_t stream);
 
+/*
+ * Attention over a paged KV cache stored with arbitrary strides (plan made
+ * without PKA_RAGGED_KV): the HND page layout [num_pages, 2, Hkv, ps, D],
+ * separate K and V pools, or pages spaced apart in a larger buffer
+ * (FlashInfer documentation, "KV-Cache Layout in FlashInfer / Layout:
+ * NHD/HND"; FlashInfer 0.2 release blog, "non-contiguous KV-cache").
+ * The K row of (page, slot, KV head) starts at element
+ *   k_cache + page * page_stride + slot * slot_stride + head * head_stride
+ * and holds head_dim contiguous bf16; its V row is at the same offset from
+ * v_cache.  Strides count bf16 elements and must be positive multiples of 8;
+ * page_stride < 2^31, slot_stride < 2^24; k_cache and v_cache 16-byte
+ * aligned (PKA_ERR_INVALID_ARG / PKA_ERR_UNSUPPORTED otherwise).  pka_run
+ * is this call with page_stride = 2*ps*Hkv*D, slot_stride = Hkv*D,
+ * head_stride = D and v_cache = k_cache + ps*Hkv*D.
+ */
+int pka_run_paged_strided(const pka_plan* plan, const void* q, const void* k_cache,
+                          const void* v_cache, int64_t page_stride, int64_t slot_stride,
+                          int64_t head_stride, void* o, float* lse, pka_stream_t stream);
+
 /* Attention over ragged dense K/V (plan made with PKA_RAGGED_KV). */
 int pka_run_ragged(const pka_plan* plan, const void* q, const void* k, const void* v, void* o,
                    float* lse, pka_stream_t stream);

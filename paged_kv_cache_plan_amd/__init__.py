@@ -36,7 +36,7 @@ PKA_KERNEL_DECODE = 1
 EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka_plan_get_info",
             "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
             "pka_debug_gather", "pka_plan_destroy", "pka_get_batch_indices_positions",
-            "pka_append_paged_kv"]
+            "pka_append_paged_kv", "pka_run_paged_strided"]
 
 
 class PlanInfo(ctypes.Structure):
@@ -92,6 +92,9 @@ def load_library(path: str = LIB_PATH):
     L.pka_merge_states.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp, vp, u32, vp]
     L.pka_debug_gather.restype = ctypes.c_int
     L.pka_debug_gather.argtypes = [vp, vp, vp, vp, vp]
+    L.pka_run_paged_strided.restype = ctypes.c_int
+    L.pka_run_paged_strided.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp,
+                                        vp]
     L.pka_get_batch_indices_positions.restype = ctypes.c_int
     L.pka_get_batch_indices_positions.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     L.pka_append_paged_kv.restype = ctypes.c_int
@@ -256,6 +259,35 @@ class Plan:
                                         _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
                                         _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
                                         _stream_ptr(stream)))
+        return o, lse
+
+    def run_strided(self, q, k_cache, v_cache, o=None, lse=None, stream=None):
+        """Attention over a paged KV cache held in strided views.
+
+        k_cache and v_cache are bf16 GPU tensors viewed as [num_pages,
+        page_size, Hkv, D] with the last dimension contiguous and any other
+        strides: for example pool[:, 0] of an NHD pool, an HND pool
+        [num_pages, 2, Hkv, ps, D] as pool[:, 0].permute(0, 2, 1, 3), or two
+        separate K and V pools.  Returns (o, lse)."""
+        import torch
+        if self.ragged:
+            raise ValueError("plan was made for ragged K/V: use run_ragged")
+        for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+            if not t.is_cuda or t.dtype != torch.bfloat16:
+                raise ValueError(f"{name} must be a bf16 GPU tensor")
+            if t.dim() != 4 or tuple(t.shape[1:]) != (self.page_size, self.num_kv_heads, self.head_dim):
+                raise ValueError(f"{name} must be viewed as [num_pages, page_size, Hkv, D]")
+            if t.stride(3) != 1:
+                raise ValueError(f"{name}: the head_dim axis must be contiguous")
+        if k_cache.stride() != v_cache.stride():
+            raise ValueError("k_cache and v_cache must have the same strides")
+        o, lse = self._outputs(q, o, lse)
+        ps_, ss, hs = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
+        _check(self._lib.pka_run_paged_strided(self._handle, _dev_ptr(q, "q", torch.bfloat16),
+                                               ctypes.c_void_p(k_cache.data_ptr()),
+                                               ctypes.c_void_p(v_cache.data_ptr()), ps_, ss, hs,
+                                               _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
+                                               _stream_ptr(stream)))
         return o, lse
 
     def debug_gather(self, paged_kv, stream=None):

@@ -107,7 +107,22 @@ int plan_or_error(const pka::PlanInput& in, pka::PlanResult* res) {
 
 bool plan_ok(const pka_plan* p) { return p && p->magic == kPlanMagic; }
 
-pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const void* v, void* o, float* lse) {
+// KV addressing: element strides between pages (ragged: tokens), slots and
+// KV heads; V rows sit at the same offsets from v as K rows from k.
+struct KvLayout {
+  int64_t page_stride, slot_stride, head_stride;
+};
+
+// The layouts of pka_run (NHD pool [num_pages, 2, ps, Hkv, D]) and
+// pka_run_ragged ([total_kv, Hkv, D] K and V).
+KvLayout standard_layout(const pka_plan* p) {
+  const int64_t row = static_cast<int64_t>(p->num_kv_heads) * p->head_dim;
+  if (p->flags & PKA_RAGGED_KV) return {row, row, p->head_dim};
+  return {2 * static_cast<int64_t>(p->page_size) * row, row, p->head_dim};
+}
+
+pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const void* v, const KvLayout& kv,
+                        void* o, float* lse) {
   pka::AttnArgs a{};
   const int32_t* iw = static_cast<const int32_t*>(p->int_ws);
   a.q = static_cast<const uint16_t*>(q);
@@ -122,12 +137,11 @@ pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const v
   a.kv_indices = iw + p->off_idx;
   a.sched = const_cast<int32_t*>(iw) + p->off_sched;
   a.num_queues = p->info.num_queues;
-  const int64_t row = static_cast<int64_t>(p->num_kv_heads) * p->head_dim;
   const bool ragged = p->flags & PKA_RAGGED_KV;
-  a.row_stride = static_cast<int32_t>(row);
   a.page_size = ragged ? 1 : p->page_size;
-  a.v_offset = ragged ? 0 : static_cast<int64_t>(p->page_size) * row;
-  a.page_stride = ragged ? row : 2 * static_cast<int64_t>(p->page_size) * row;
+  a.page_stride = kv.page_stride;
+  a.row_stride = static_cast<int32_t>(kv.slot_stride);
+  a.head_stride = kv.head_stride;
   int shift = -1;
   for (int s = 0; s < 8; ++s)
     if ((1 << s) == a.page_size) shift = s;
@@ -139,12 +153,12 @@ pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const v
   return a;
 }
 
-int run_common(const pka_plan* p, const void* q, const void* k, const void* v, void* o, float* lse,
-               hipStream_t stream) {
+int run_common(const pka_plan* p, const void* q, const void* k, const void* v, const KvLayout& kv, void* o,
+               float* lse, hipStream_t stream) {
   if (p->info.total_q == 0) return PKA_OK;
   if (!q || !o) return set_error(PKA_ERR_INVALID_ARG, "q and o must not be NULL");
   if (p->info.total_kv > 0 && !k) return set_error(PKA_ERR_INVALID_ARG, "KV pointer must not be NULL");
-  const pka::AttnArgs a = attn_args(p, q, k, v, o, lse);
+  const pka::AttnArgs a = attn_args(p, q, k, v, kv, o, lse);
   const bool paged = !(p->flags & PKA_RAGGED_KV);
   hipError_t e;
   if (p->info.kernel == PKA_KERNEL_DECODE)
@@ -298,7 +312,28 @@ int pka_run(const pka_plan* plan, const void* q, const void* paged_kv, void* o, 
   if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
   if (plan->flags & PKA_RAGGED_KV)
     return set_error(PKA_ERR_INVALID_ARG, "plan was made with PKA_RAGGED_KV: use pka_run_ragged");
-  return run_common(plan, q, paged_kv, nullptr, o, lse, stream);
+  const int64_t half = static_cast<int64_t>(plan->page_size) * plan->num_kv_heads * plan->head_dim;
+  const void* v = paged_kv ? static_cast<const uint16_t*>(paged_kv) + half : nullptr;
+  return run_common(plan, q, paged_kv, v, standard_layout(plan), o, lse, stream);
+}
+
+int pka_run_paged_strided(const pka_plan* plan, const void* q, const void* k_cache, const void* v_cache,
+                          int64_t page_stride, int64_t slot_stride, int64_t head_stride, void* o, float* lse,
+                          pka_stream_t stream) {
+  if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
+  if (plan->flags & PKA_RAGGED_KV)
+    return set_error(PKA_ERR_INVALID_ARG, "plan was made with PKA_RAGGED_KV: use pka_run_ragged");
+  if (plan->info.total_kv > 0 && (!k_cache || !v_cache))
+    return set_error(PKA_ERR_INVALID_ARG, "k_cache and v_cache must not be NULL");
+  if (page_stride <= 0 || slot_stride <= 0 || head_stride <= 0 || page_stride % 8 || slot_stride % 8 ||
+      head_stride % 8)
+    return set_error(PKA_ERR_INVALID_ARG, "strides must be positive multiples of 8 elements");
+  if (page_stride >= (int64_t(1) << 31) || slot_stride >= (int64_t(1) << 24))
+    return set_error(PKA_ERR_UNSUPPORTED, "page stride must be < 2^31 and slot stride < 2^24 elements");
+  for (const void* ptr : {k_cache, v_cache})
+    if (ptr && reinterpret_cast<uintptr_t>(ptr) % 16 != 0)
+      return set_error(PKA_ERR_INVALID_ARG, "k_cache and v_cache must be 16-byte aligned");
+  return run_common(plan, q, k_cache, v_cache, {page_stride, slot_stride, head_stride}, o, lse, stream);
 }
 
 int pka_run_ragged(const pka_plan* plan, const void* q, const void* k, const void* v, void* o, float* lse,
@@ -307,7 +342,7 @@ int pka_run_ragged(const pka_plan* plan, const void* q, const void* k, const voi
   if (!(plan->flags & PKA_RAGGED_KV))
     return set_error(PKA_ERR_INVALID_ARG, "plan was made for a paged KV cache: use pka_run");
   if (plan->info.total_kv > 0 && !v) return set_error(PKA_ERR_INVALID_ARG, "v must not be NULL");
-  return run_common(plan, q, k, v, o, lse, stream);
+  return run_common(plan, q, k, v, standard_layout(plan), o, lse, stream);
 }
 
 int pka_merge_states(const float* v, const float* s, int64_t n, int32_t num_states, int32_t num_heads,

@@ -9,8 +9,11 @@ namespace pka {
 // count bf16 elements.
 struct AttnArgs {
   const uint16_t* q;         // bf16 [total_q, Hq, D]
-  const uint16_t* k;         // paged: pool [num_pages, 2, ps, Hkv, D]; ragged: K [total_kv, Hkv, D]
-  const uint16_t* v;         // ragged: V [total_kv, Hkv, D]; paged: unused
+  // K row of (page or token p, slot s, KV head h): k + p * page_stride +
+  // s * row_stride + h * head_stride, D contiguous elements; V rows at the
+  // same offsets from v.  Ragged: p is the token row and s = 0.
+  const uint16_t* k;
+  const uint16_t* v;
   void* o;                   // bf16 or fp32 [total_q, Hq, D]
   float* lse;                // fp32 [total_q, Hq] or null
   float* part_o;             // fp32 [num_partial_rows, D]
@@ -19,9 +22,9 @@ struct AttnArgs {
   const int32_t* req;        // [batch][8]
   const int32_t* kv_indices; // [nnz] device copy
   int32_t* sched;            // prefill: [num_queues][64] queue records with their counters
-  int64_t page_stride;       // elements per page: 2 * ps * Hkv * D
-  int64_t v_offset;          // elements from a K row to its V row: ps * Hkv * D (paged)
-  int32_t row_stride;        // elements between consecutive slots / tokens: Hkv * D
+  int64_t page_stride;       // elements between pages (ragged: between tokens)
+  int64_t head_stride;       // elements between KV heads
+  int32_t row_stride;        // elements between consecutive slots of a page
   int32_t num_qo_heads;
   int32_t group;             // Hq / Hkv
   int32_t page_size;

@@ -77,8 +77,8 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 
   const int ps = a.page_size, pshift = a.page_shift;
   constexpr bool scalar_ids = MODE == kPagedUniform;
-  const uint16_t* kb_ptr = a.k + hk * D;
-  const uint16_t* vb_ptr = PAGED ? kb_ptr + a.v_offset : a.v + hk * D;
+  const uint16_t* kb_ptr = a.k + hk * a.head_stride;
+  const uint16_t* vb_ptr = a.v + hk * a.head_stride;
 
   // V loader: lane handles chunk vc of the 8 keys in slot group vg.
   const int vc = lane % CPR, vg = lane / CPR;
@@ -119,7 +119,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
       return static_cast<int64_t>(pid) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride;
     } else {
-      return static_cast<int64_t>(kv_base + key) * a.row_stride;
+      return static_cast<int64_t>(kv_base + key) * a.page_stride;
     }
   };
   struct Data { u32x4 k[2][DS]; u32x4 v[8]; };

@@ -185,7 +185,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
       return static_cast<uint64_t>(static_cast<uint32_t>(pid)) * page_bytes +
              static_cast<uint32_t>(slot_of(key)) * row_bytes;
     } else {
-      return static_cast<uint64_t>(static_cast<uint32_t>(U.kv_base + key)) * row_bytes;
+      return static_cast<uint64_t>(static_cast<uint32_t>(U.kv_base + key)) * page_bytes;
     }
   };
   auto fetch_data = [&](const UnitInfo& U, int k0, const int* ids_in) {
@@ -198,9 +198,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
       pair[1] = (lc & 1) ? ids_in[0] : other;
       ids = pair;
     }
-    const char* kbase = reinterpret_cast<const char*>(a.k + U.hk * D + 8 * lc);
-    const char* vbase =
-        PAGED ? kbase + a.v_offset * 2 : reinterpret_cast<const char*>(a.v + U.hk * D + 8 * lc);
+    const char* kbase = reinterpret_cast<const char*>(a.k + U.hk * a.head_stride + 8 * lc);
+    const char* vbase = reinterpret_cast<const char*>(a.v + U.hk * a.head_stride + 8 * lc);
     const int key0 = k0 + KPT * lj;
     if (k0 + kBN <= U.kv_hi) {  // uniform: the whole tile is in range
       if constexpr (one_page) {
