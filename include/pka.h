@@ -192,6 +192,19 @@ int pka_merge_states(const float* v, const float* s, int64_t n, int32_t num_stat
                      uint32_t flags, pka_stream_t stream);
 
 /*
+ * pka_merge_states over states at arbitrary strides (counted in floats):
+ * state s of row i, head h is v[i*v_row_stride + s*v_state_stride + h*D ..]
+ * and s[i*s_row_stride + s*s_state_stride + h].  Used by cascade attention,
+ * whose levels write their states as [S, n, H, D] (FlashInfer documentation,
+ * "flashinfer.cascade: Cascade Attention"; the merge is the one above).
+ * v strides must be multiples of 4; v and v_out 16-byte aligned.
+ */
+int pka_merge_states_strided(const float* v, const float* s, int64_t n, int32_t num_states,
+                             int32_t num_heads, int32_t head_dim, int64_t v_row_stride,
+                             int64_t v_state_stride, int64_t s_row_stride, int64_t s_state_stride,
+                             void* v_out, float* s_out, uint32_t flags, pka_stream_t stream);
+
+/*
  * Test aid: copy the keys and values the page table selects into dense
  * k_dense / v_dense bf16 [total_kv, num_kv_heads, head_dim] (requests in
  * order, each kv_len rows), exactly as the attention kernels address them.

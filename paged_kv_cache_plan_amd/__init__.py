@@ -36,7 +36,7 @@ PKA_KERNEL_DECODE = 1
 EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka_plan_get_info",
             "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
             "pka_debug_gather", "pka_plan_destroy", "pka_get_batch_indices_positions",
-            "pka_append_paged_kv", "pka_run_paged_strided"]
+            "pka_append_paged_kv", "pka_run_paged_strided", "pka_merge_states_strided"]
 
 
 class PlanInfo(ctypes.Structure):
@@ -92,6 +92,9 @@ def load_library(path: str = LIB_PATH):
     L.pka_merge_states.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp, vp, u32, vp]
     L.pka_debug_gather.restype = ctypes.c_int
     L.pka_debug_gather.argtypes = [vp, vp, vp, vp, vp]
+    L.pka_merge_states_strided.restype = ctypes.c_int
+    L.pka_merge_states_strided.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, ctypes.c_int64, ctypes.c_int64,
+                                           ctypes.c_int64, ctypes.c_int64, vp, vp, u32, vp]
     L.pka_run_paged_strided.restype = ctypes.c_int
     L.pka_run_paged_strided.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp,
                                         vp]
@@ -327,6 +330,70 @@ def merge_states(v, s, out_fp32=True, stream=None):
                               _dev_ptr(v_out, "v_out"), _dev_ptr(s_out, "s_out"),
                               PKA_OUT_FP32 if out_fp32 else 0, _stream_ptr(stream)))
     return v_out, s_out
+
+
+def merge_states_levels(v, s, out_fp32=False, stream=None):
+    """Merge states stored level-major: v fp32 [S, n, H, D], s fp32 [S, n, H]
+    (each contiguous) -> (v_out [n, H, D], s_out [n, H])."""
+    import torch
+    L = load_library()
+    S, n, H, D = v.shape
+    if tuple(s.shape) != (S, n, H) or not v.is_contiguous() or not s.is_contiguous():
+        raise ValueError("v must be contiguous [S, n, H, D] and s contiguous [S, n, H]")
+    v_out = torch.empty((n, H, D), dtype=torch.float32 if out_fp32 else torch.bfloat16, device=v.device)
+    s_out = torch.empty((n, H), dtype=torch.float32, device=v.device)
+    _check(L.pka_merge_states_strided(_dev_ptr(v, "v", torch.float32), _dev_ptr(s, "s", torch.float32), n, S, H, D,
+                                      H * D, n * H * D, H, n * H, _dev_ptr(v_out, "v_out"),
+                                      _dev_ptr(s_out, "s_out"), PKA_OUT_FP32 if out_fp32 else 0,
+                                      _stream_ptr(stream)))
+    return v_out, s_out
+
+
+class Cascade:
+    """Multi-level cascade attention over one paged KV pool (FlashInfer
+    documentation, "flashinfer.cascade: Cascade Attention" and "Multi-level
+    Cascade Inference Data Layout").
+
+    ``levels`` is a list of (qo_indptr, kv_indptr, kv_indices,
+    kv_last_page_len): level l groups the same total_q query rows into
+    contiguous groups (its qo_indptr) that share the keys of its page table.
+    A query attends to the concatenation of its groups' keys, level 0 first.
+    Only the last level is masked (bottom-right causal when ``causal``); the
+    keys of earlier levels precede every query, so each request's last-level
+    keys must include its own query tokens (at least qo_len keys).  Each level is one plan and
+    run writing an fp32 state into a [levels, total_q, Hq, D] buffer, and
+    pka_merge_states_strided merges them (the recursive-attention identity).
+    """
+
+    def __init__(self, levels, num_qo_heads, num_kv_heads, head_dim, page_size, causal=True, sm_scale=-1.0,
+                 num_pages=None, out_fp32=False, device=None, stream=None):
+        n = len(levels)
+        if n < 1:
+            raise ValueError("at least one level")
+        self.plans = []
+        for i, (qo, kvp, kvi, last) in enumerate(levels):
+            self.plans.append(Plan(qo, kvp, kvi, last, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                   causal=causal and i == n - 1, sm_scale=sm_scale, num_pages=num_pages,
+                                   out_fp32=True, device=device, stream=stream))
+        totals = {p.total_q for p in self.plans}
+        if len(totals) != 1:
+            raise ValueError("every level must cover the same query rows")
+        self.total_q = totals.pop()
+        self.num_qo_heads, self.head_dim, self.out_fp32 = num_qo_heads, head_dim, out_fp32
+
+    def run(self, q, paged_kv, stream=None):
+        """Returns (o, lse) of the cascade."""
+        import torch
+        S = len(self.plans)
+        v = torch.empty((S, self.total_q, self.num_qo_heads, self.head_dim), dtype=torch.float32, device=q.device)
+        s = torch.empty((S, self.total_q, self.num_qo_heads), dtype=torch.float32, device=q.device)
+        for i, p in enumerate(self.plans):
+            p.run(q, paged_kv, o=v[i], lse=s[i], stream=stream)
+        return merge_states_levels(v, s, out_fp32=self.out_fp32, stream=stream)
+
+    def close(self):
+        for p in self.plans:
+            p.close()
 
 
 def get_batch_indices_positions(append_indptr, seq_lens, nnz, stream=None):

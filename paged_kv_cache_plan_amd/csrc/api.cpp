@@ -347,14 +347,32 @@ int pka_run_ragged(const pka_plan* plan, const void* q, const void* k, const voi
 
 int pka_merge_states(const float* v, const float* s, int64_t n, int32_t num_states, int32_t num_heads,
                      int32_t head_dim, void* v_out, float* s_out, uint32_t flags, pka_stream_t stream) {
+  const int64_t S = num_states, H = num_heads, D = head_dim;
+  return pka_merge_states_strided(v, s, n, num_states, num_heads, head_dim, S * H * D, H * D, S * H, H, v_out,
+                                  s_out, flags, stream);
+}
+
+int pka_merge_states_strided(const float* v, const float* s, int64_t n, int32_t num_states, int32_t num_heads,
+                             int32_t head_dim, int64_t v_row_stride, int64_t v_state_stride,
+                             int64_t s_row_stride, int64_t s_state_stride, void* v_out, float* s_out,
+                             uint32_t flags, pka_stream_t stream) {
   if (n < 0 || num_states < 1 || num_heads < 1 || head_dim < 4 || head_dim % 4 != 0 || head_dim > 1024)
     return set_error(PKA_ERR_INVALID_ARG, "merge_states: bad sizes");
+  if (v_row_stride < 0 || v_state_stride < 0 || s_row_stride < 0 || s_state_stride < 0 || v_row_stride % 4 ||
+      v_state_stride % 4)
+    return set_error(PKA_ERR_INVALID_ARG, "merge_states: v strides must be non-negative multiples of 4");
+  if ((v && reinterpret_cast<uintptr_t>(v) % 16) || (v_out && reinterpret_cast<uintptr_t>(v_out) % 16))
+    return set_error(PKA_ERR_INVALID_ARG, "merge_states: v and v_out must be 16-byte aligned");
   if (flags & ~uint32_t(PKA_OUT_FP32)) return set_error(PKA_ERR_INVALID_ARG, "merge_states: unknown flags");
   if (n == 0) return PKA_OK;
   if (!v || !s || !v_out) return set_error(PKA_ERR_INVALID_ARG, "merge_states: null pointer");
   pka::MergeStatesArgs a{};
   a.v = v;
   a.s = s;
+  a.v_row_stride = v_row_stride;
+  a.v_state_stride = v_state_stride;
+  a.s_row_stride = s_row_stride;
+  a.s_state_stride = s_state_stride;
   a.v_out = v_out;
   a.s_out = s_out;
   a.n = n;

@@ -47,10 +47,17 @@ struct MergeArgs {
   int32_t out_fp32;
 };
 
-// Arguments of the standalone merge of attention states.
+// Arguments of the standalone merge of attention states.  State s of row i,
+// head h: v + i * v_row_stride + s * v_state_stride + h * D (D floats) and
+// s + i * s_row_stride + s * s_state_stride + h; by default [n, S, H, D] and
+// [n, S, H].
 struct MergeStatesArgs {
-  const float* v;            // [n, S, H, D]
-  const float* s;            // [n, S, H]
+  const float* v;
+  const float* s;
+  int64_t v_row_stride;
+  int64_t v_state_stride;
+  int64_t s_row_stride;
+  int64_t s_state_stride;
   void* v_out;               // [n, H, D]
   float* s_out;              // [n, H] or null
   int64_t n;

@@ -74,17 +74,18 @@ __global__ __launch_bounds__(kThreads) void merge_states_kernel(MergeStatesArgs 
     const int64_t nh = it / C4;
     const int h = static_cast<int>(nh % H);
     const int64_t i = nh / H;
-    const float* sp = a.s + i * S * H + h;
+    const float* sp = a.s + i * a.s_row_stride + h;
+    const float* vp = a.v + i * a.v_row_stride + static_cast<int64_t>(h) * D + 4 * c4;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, sp[static_cast<int64_t>(s) * H]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, sp[s * a.s_state_stride]);
     float W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
       for (int s = 0; s < S; ++s) {
-        const float w = fast_exp2(sp[static_cast<int64_t>(s) * H] - M);
+        const float w = fast_exp2(sp[s * a.s_state_stride] - M);
         if (w > 0.f) {
           W += w;
-          acc += w * *reinterpret_cast<const f32x4*>(a.v + ((i * S + s) * H + h) * D + 4 * c4);
+          acc += w * *reinterpret_cast<const f32x4*>(vp + s * a.v_state_stride);
         }
       }
     }

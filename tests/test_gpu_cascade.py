@@ -1,0 +1,108 @@
+"""Cascade attention (pka.Cascade: one plan and run per level, merged by
+pka_merge_states_strided) against the oracle run on the concatenation of each
+request's keys, level 0 first, with the bottom-right causal mask over the
+whole length -- the recursive-attention identity says the two agree."""
+import pytest
+import torch
+
+import oracle
+import paged_kv_cache_plan_amd as pka
+from tests.gpu_common import compare, cuda
+
+pytestmark = pytest.mark.gpu
+
+
+def _pages(n_tokens, ps, free):
+    n = (n_tokens + ps - 1) // ps
+    ids, free[:] = free[:n], free[n:]
+    last = 0 if n_tokens == 0 else n_tokens - (n - 1) * ps
+    return ids, last
+
+
+def _build(seed, groups_per_level, level_lens, qo_lens, ps=16, Hq=8, Hkv=2, D=128):
+    """groups_per_level[l]: list of request-index lists (contiguous, covering
+    all requests); level_lens[l][g]: key count of group g at level l (the last
+    level has one group per request)."""
+    g = torch.Generator().manual_seed(seed)
+    B = len(qo_lens)
+    total_tokens = sum(sum(x) for x in level_lens)
+    num_pages = sum((t + ps - 1) // ps for lens in level_lens for t in lens) + 8
+    free = torch.randperm(num_pages, generator=g).tolist()
+    pool = torch.randn((num_pages, 2, ps, Hkv, D), generator=g).to(torch.bfloat16)
+    qo_indptr_req = [0]
+    for n in qo_lens:
+        qo_indptr_req.append(qo_indptr_req[-1] + n)
+    total_q = qo_indptr_req[-1]
+    q = torch.randn((total_q, Hq, D), generator=g).to(torch.bfloat16)
+    levels, level_tables = [], []
+    for groups, lens in zip(groups_per_level, level_lens):
+        qo = [0]
+        kvp, kvi, last = [0], [], []
+        for members, n_tok in zip(groups, lens):
+            qo.append(qo_indptr_req[members[-1] + 1])
+            ids, l_ = _pages(n_tok, ps, free)
+            kvi += ids
+            kvp.append(len(kvi))
+            last.append(l_)
+        t = (torch.tensor(qo, dtype=torch.int32), torch.tensor(kvp, dtype=torch.int32),
+             torch.tensor(kvi, dtype=torch.int32), torch.tensor(last, dtype=torch.int32))
+        levels.append(t)
+        level_tables.append((groups, t))
+    return pool, q, levels, level_tables, torch.tensor(qo_indptr_req, dtype=torch.int32), num_pages, (Hq, Hkv, D, ps)
+
+
+def _oracle(pool, q, level_tables, qo_indptr, causal, ps):
+    def kv_source(r):
+        Ks, Vs = [], []
+        for groups, (qo, kvp, kvi, last) in level_tables:
+            gi = next(i for i, m in enumerate(groups) if r in m)
+            K, V = oracle.gather_paged_kv(pool, kvp, kvi, last, ps, gi)
+            Ks.append(K)
+            Vs.append(V)
+        return torch.cat(Ks), torch.cat(Vs)
+    return oracle.batch_attention(q, qo_indptr, kv_source, pool.shape[3], causal)
+
+
+@pytest.mark.parametrize("qo", ["prefill", "decode"])
+def test_two_level_shared_prefix(qo):
+    B = 5
+    qo_lens = [1] * B if qo == "decode" else [37, 1, 90, 64, 5]
+    own = [70, 3, 130, 64, 18]
+    own = [max(o, n) for o, n in zip(own, qo_lens)]
+    groups = [[list(range(B))], [[r] for r in range(B)]]
+    pool, q, levels, tables, qo_indptr, num_pages, (Hq, Hkv, D, ps) = _build(1, groups, [[300], own], qo_lens)
+    dev = cuda()
+    c = pka.Cascade(levels, Hq, Hkv, D, ps, causal=True, num_pages=num_pages, device=dev)
+    o, lse = c.run(q.to(dev), pool.to(dev))
+    torch.cuda.synchronize()
+    c.close()
+    compare(o.float().cpu(), lse.cpu(), *_oracle(pool, q, tables, qo_indptr, True, ps), f"cascade-2 {qo}")
+
+
+def test_three_levels_uneven_pages():
+    """Level 0 shared by all, level 1 by two groups, level 2 per request;
+    key counts not multiples of the page size at every level."""
+    B = 4
+    qo_lens = [20, 33, 7, 50]
+    groups = [[[0, 1, 2, 3]], [[0, 1], [2, 3]], [[0], [1], [2], [3]]]
+    lens = [[45], [19, 100], [20, 40, 9, 77]]
+    pool, q, levels, tables, qo_indptr, num_pages, (Hq, Hkv, D, ps) = _build(2, groups, lens, qo_lens)
+    dev = cuda()
+    c = pka.Cascade(levels, Hq, Hkv, D, ps, causal=True, num_pages=num_pages, out_fp32=True, device=dev)
+    o, lse = c.run(q.to(dev), pool.to(dev))
+    torch.cuda.synchronize()
+    c.close()
+    compare(o.cpu(), lse.cpu(), *_oracle(pool, q, tables, qo_indptr, True, ps), "cascade-3")
+
+
+def test_merge_states_levels():
+    g = torch.Generator().manual_seed(3)
+    S, n, H, D = 3, 41, 4, 64
+    v = torch.randn((S, n, H, D), generator=g)
+    s = torch.randn((S, n, H), generator=g) * 4
+    s[1, 5] = float("-inf")
+    s[:, 7, 2] = float("-inf")
+    dev = cuda()
+    vo, so = pka.merge_states_levels(v.to(dev), s.to(dev), out_fp32=True)
+    ro, rs = oracle.merge_states(v.permute(1, 0, 2, 3).double(), s.permute(1, 0, 2).double())
+    compare(vo.cpu(), so.cpu(), ro, rs, "merge levels")
