@@ -68,6 +68,11 @@ enum {
 #define PKA_RAGGED_KV 0x4u        /* K/V are ragged dense tensors: kv_indptr counts tokens,
                                      kv_indices and kv_last_page_len are unused (may be NULL),
                                      page_size is ignored; run with pka_run_ragged           */
+#define PKA_GRAPH_STABLE 0x8u     /* every run enqueues the same launches whatever the batch, so
+                                     a run captured into a HIP graph can be replayed after
+                                     pka_plan_update has planned another batch into the same
+                                     workspaces (FlashInfer 0.2 release blog, "CUDAGraph
+                                     compatibility for variable-length inputs")              */
 
 /* Which attention kernel a plan launches. */
 enum { PKA_KERNEL_PREFILL = 0, PKA_KERNEL_DECODE = 1 };
@@ -253,6 +258,20 @@ int pka_append_paged_kv(const void* append_k, const void* append_v, const int32_
                         int32_t page_size, int32_t num_kv_heads, int32_t head_dim,
                         const int32_t* kv_indices, const int32_t* kv_indptr, int32_t batch,
                         pka_stream_t stream);
+
+/*
+ * Plan another batch into an existing plan's workspaces (same heads,
+ * head_dim, page_size, pool, causal flag, sm_scale and flags; host arrays as
+ * for pka_plan_create).  The new image is uploaded on `stream`; runs ordered
+ * after it on that stream see the new batch, and a graph-stable plan's
+ * captured runs replay it.  The call waits for the plan's previous upload
+ * (a host copy only, never for kernels).  The workspaces given at creation
+ * must be large enough (PKA_ERR_WORKSPACE); a graph-stable plan cannot move
+ * between prefill and decode batches (PKA_ERR_INVALID_ARG).
+ */
+int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
+                    const int32_t* kv_indices, const int32_t* kv_last_page_len, int32_t batch,
+                    int32_t nnz_pages, pka_stream_t stream);
 
 /* Free a plan.  The caller must first make sure the plan's copy and every run
  * using it have completed (for example by synchronising the stream).  NULL is

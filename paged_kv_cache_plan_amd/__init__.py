@@ -29,6 +29,7 @@ PKA_ERR_HIP = 4
 PKA_DISABLE_SPLIT_KV = 0x1
 PKA_OUT_FP32 = 0x2
 PKA_RAGGED_KV = 0x4
+PKA_GRAPH_STABLE = 0x8
 
 PKA_KERNEL_PREFILL = 0
 PKA_KERNEL_DECODE = 1
@@ -36,7 +37,8 @@ PKA_KERNEL_DECODE = 1
 EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka_plan_get_info",
             "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
             "pka_debug_gather", "pka_plan_destroy", "pka_get_batch_indices_positions",
-            "pka_append_paged_kv", "pka_run_paged_strided", "pka_merge_states_strided"]
+            "pka_append_paged_kv", "pka_run_paged_strided", "pka_merge_states_strided",
+            "pka_plan_update"]
 
 
 class PlanInfo(ctypes.Structure):
@@ -102,6 +104,8 @@ def load_library(path: str = LIB_PATH):
     L.pka_get_batch_indices_positions.argtypes = [vp, vp, i32, i32, vp, vp, vp]
     L.pka_append_paged_kv.restype = ctypes.c_int
     L.pka_append_paged_kv.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, vp]
+    L.pka_plan_update.restype = ctypes.c_int
+    L.pka_plan_update.argtypes = [vp, i32p, i32p, i32p, i32p, i32, i32, vp]
     L.pka_plan_destroy.restype = None
     L.pka_plan_destroy.argtypes = [vp]
     _lib = L
@@ -185,19 +189,23 @@ class Plan:
 
     Index arrays are host tensors (copied during the call).  The plan uploads
     its work arrays with one asynchronous copy on ``stream`` (default: the
-    current stream) and does not synchronise.
+    current stream) and does not synchronise.  ``graph_stable`` plans enqueue
+    the same launches for every batch, so a captured run can be replayed
+    after ``update``; size their workspaces for the largest batch with
+    ``int_ws_bytes`` / ``float_ws_bytes`` (at least what this batch needs is
+    allocated).
     """
 
     def __init__(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads,
                  num_kv_heads, head_dim, page_size=1, causal=True, sm_scale=None,
                  num_pages=None, ragged=False, disable_split_kv=False, out_fp32=False,
-                 device=None, stream=None):
+                 device=None, stream=None, graph_stable=False, int_ws_bytes=0, float_ws_bytes=0):
         import torch
         L = load_library()
         self._lib = L
         self._handle = ctypes.c_void_p()
         flags = (PKA_RAGGED_KV if ragged else 0) | (PKA_DISABLE_SPLIT_KV if disable_split_kv else 0) \
-            | (PKA_OUT_FP32 if out_fp32 else 0)
+            | (PKA_OUT_FP32 if out_fp32 else 0) | (PKA_GRAPH_STABLE if graph_stable else 0)
         self.flags = flags
         self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
         self.page_size = page_size
@@ -218,20 +226,35 @@ class Plan:
         _check(L.pka_plan_workspace_size(qo_p, kv_p, last_p, B, num_qo_heads, num_kv_heads, head_dim,
                                          page_size, int(bool(causal)), flags, ctypes.byref(a),
                                          ctypes.byref(b)))
-        self.int_ws = torch.empty(a.value, dtype=torch.uint8, device=dev)
-        self.float_ws = torch.empty(b.value, dtype=torch.uint8, device=dev)
+        ia, fb = max(a.value, int(int_ws_bytes)), max(b.value, int(float_ws_bytes))
+        self.int_ws = torch.empty(ia, dtype=torch.uint8, device=dev)
+        self.float_ws = torch.empty(fb, dtype=torch.uint8, device=dev)
         self._stream = stream if stream is not None else torch.cuda.current_stream(dev)
         _check(L.pka_plan_create(qo_p, kv_p, idx_p, last_p, B, nnz, num_pages, num_qo_heads,
                                  num_kv_heads, head_dim, page_size, int(bool(causal)),
                                  float(sm_scale) if sm_scale else 0.0, flags,
-                                 ctypes.c_void_p(self.int_ws.data_ptr()), a.value,
-                                 ctypes.c_void_p(self.float_ws.data_ptr()), b.value,
+                                 ctypes.c_void_p(self.int_ws.data_ptr()), ia,
+                                 ctypes.c_void_p(self.float_ws.data_ptr()), fb,
                                  _stream_ptr(self._stream), ctypes.byref(self._handle)))
         info = PlanInfo()
         _check(L.pka_plan_get_info(self._handle, ctypes.byref(info)))
         self.info = info.as_dict()
         self.total_q = info.total_q
         self.device = dev
+
+    def update(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, stream=None):
+        """Plan another batch into this plan's workspaces (pka_plan_update)."""
+        qo, qo_p = _host_i32(qo_indptr)
+        kv, kv_p = _host_i32(kv_indptr)
+        idx, idx_p = (None, None) if self.ragged else _host_i32(kv_indices)
+        last, last_p = (None, None) if self.ragged else _host_i32(kv_last_page_len)
+        nnz = 0 if idx is None else idx.numel()
+        _check(self._lib.pka_plan_update(self._handle, qo_p, kv_p, idx_p, last_p, qo.numel() - 1, nnz,
+                                         _stream_ptr(stream if stream is not None else self._stream)))
+        info = PlanInfo()
+        _check(self._lib.pka_plan_get_info(self._handle, ctypes.byref(info)))
+        self.info = info.as_dict()
+        self.total_q = info.total_q
 
     def _outputs(self, q, o, lse):
         import torch

@@ -33,7 +33,7 @@ int hip_error(const char* what, hipError_t e) {
 }
 
 constexpr uint32_t kPlanMagic = 0x4e4c5050u;  // "PPLN"
-constexpr uint32_t kKnownFlags = PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV;
+constexpr uint32_t kKnownFlags = PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV | PKA_GRAPH_STABLE;
 
 int env_int(const char* name) {
   const char* s = std::getenv(name);
@@ -52,7 +52,10 @@ struct pka_plan {
   void* float_ws;
   size_t partial_lse_offset;
   int32_t off_units, off_req, off_merge, off_idx, off_sched;
-  void* staging;  // pinned copy of the image, read by the enqueued copy
+  size_t int_ws_bytes, float_ws_bytes;  // capacities of the caller's workspaces
+  void* staging;        // pinned copy of the image, read by the enqueued copy
+  size_t staging_bytes;
+  hipEvent_t uploaded;  // recorded after the image copy
 };
 
 namespace {
@@ -107,6 +110,38 @@ int plan_or_error(const pka::PlanInput& in, pka::PlanResult* res) {
 
 bool plan_ok(const pka_plan* p) { return p && p->magic == kPlanMagic; }
 
+// Copy a planned image into the plan's pinned staging and enqueue its upload
+// to the int workspace; the staging is reused once the previous upload has
+// completed (host waits on that copy only, never on kernels).
+int upload(pka_plan* p, const pka::PlanResult& res, int32_t batch, int32_t nnz, hipStream_t stream) {
+  const size_t need = res.image.size() * sizeof(int32_t);
+  if (p->staging) {
+    const hipError_t w = hipEventSynchronize(p->uploaded);
+    if (w != hipSuccess) return hip_error("hipEventSynchronize(previous plan upload)", w);
+  }
+  if (need > p->staging_bytes) {
+    if (p->staging) (void)hipHostFree(p->staging);
+    p->staging = nullptr;
+    p->staging_bytes = 0;
+    const hipError_t a = hipHostMalloc(&p->staging, need, hipHostMallocDefault);
+    if (a != hipSuccess) return hip_error("hipHostMalloc(plan staging)", a);
+    p->staging_bytes = need;
+  }
+  std::memcpy(p->staging, res.image.data(), need);
+  hipError_t e = hipMemcpyAsync(p->int_ws, p->staging, need, hipMemcpyHostToDevice, stream);
+  if (e != hipSuccess) return hip_error("hipMemcpyAsync(plan upload)", e);
+  e = hipEventRecord(p->uploaded, stream);
+  if (e != hipSuccess) return hip_error("hipEventRecord(plan upload)", e);
+  fill_info(res, batch, nnz, &p->info);
+  p->partial_lse_offset = res.partial_lse_offset;
+  p->off_units = res.image[pka::kHdrOffUnits];
+  p->off_req = res.image[pka::kHdrOffReq];
+  p->off_merge = res.image[pka::kHdrOffMerge];
+  p->off_idx = res.image[pka::kHdrOffIndices];
+  p->off_sched = res.image[pka::kHdrOffSched];
+  return PKA_OK;
+}
+
 // KV addressing: element strides between pages (ragged: tokens), slots and
 // KV heads; V rows sit at the same offsets from v as K rows from k.
 struct KvLayout {
@@ -131,12 +166,7 @@ pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const v
   a.o = o;
   a.lse = lse;
   a.part_o = static_cast<float*>(p->float_ws);
-  a.part_lse = reinterpret_cast<float*>(static_cast<char*>(p->float_ws) + p->partial_lse_offset);
-  a.units = iw + p->off_units;
-  a.req = iw + p->off_req;
-  a.kv_indices = iw + p->off_idx;
-  a.sched = const_cast<int32_t*>(iw) + p->off_sched;
-  a.num_queues = p->info.num_queues;
+  a.ws = const_cast<int32_t*>(iw);
   const bool ragged = p->flags & PKA_RAGGED_KV;
   a.page_size = ragged ? 1 : p->page_size;
   a.page_stride = kv.page_stride;
@@ -155,29 +185,30 @@ pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const v
 
 int run_common(const pka_plan* p, const void* q, const void* k, const void* v, const KvLayout& kv, void* o,
                float* lse, hipStream_t stream) {
-  if (p->info.total_q == 0) return PKA_OK;
+  // A graph-stable plan always enqueues the same launches (a captured run is
+  // replayed for later batches); the kernels find an empty batch empty.
+  const bool stable = (p->flags & PKA_GRAPH_STABLE) != 0;
+  if (p->info.total_q == 0 && !stable) return PKA_OK;
   if (!q || !o) return set_error(PKA_ERR_INVALID_ARG, "q and o must not be NULL");
   if (p->info.total_kv > 0 && !k) return set_error(PKA_ERR_INVALID_ARG, "KV pointer must not be NULL");
   const pka::AttnArgs a = attn_args(p, q, k, v, kv, o, lse);
   const bool paged = !(p->flags & PKA_RAGGED_KV);
   hipError_t e;
   if (p->info.kernel == PKA_KERNEL_DECODE)
-    e = pka::launch_decode(a, p->head_dim, paged, p->info.num_units, stream);
+    e = pka::launch_decode(a, p->head_dim, paged, p->info.num_workers, stream);
   else
     e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, p->info.num_workers, stream);
   if (e != hipSuccess) return hip_error("attention launch", e);
-  if (p->info.num_merge_groups > 0) {
+  if (p->info.num_merge_groups > 0 || stable) {
     pka::MergeArgs m{};
     m.part_o = a.part_o;
-    m.part_lse = a.part_lse;
-    m.groups = static_cast<const int32_t*>(p->int_ws) + p->off_merge;
-    m.req = a.req;
+    m.ws = a.ws;
     m.o = o;
     m.lse = lse;
     m.num_qo_heads = p->num_qo_heads;
     m.group = p->group;
     m.out_fp32 = a.out_fp32;
-    e = pka::launch_merge(m, p->head_dim, p->info.num_merge_groups, stream);
+    e = pka::launch_merge(m, p->head_dim, stable ? pka::kMergeGrid : p->info.num_merge_groups, stream);
     if (e != hipSuccess) return hip_error("merge launch", e);
   }
   return PKA_OK;
@@ -259,7 +290,6 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
                                               " bytes, needs " + std::to_string(res.float_ws_bytes));
     pka_plan* p = new pka_plan{};
     p->magic = kPlanMagic;
-    fill_info(res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, &p->info);
     p->num_qo_heads = num_qo_heads;
     p->num_kv_heads = num_kv_heads;
     p->head_dim = head_dim;
@@ -271,24 +301,21 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     p->sm_scale = sm_scale > 0.f ? sm_scale : 1.0f / std::sqrt(static_cast<float>(head_dim));
     p->int_ws = int_ws;
     p->float_ws = float_ws;
-    p->partial_lse_offset = res.partial_lse_offset;
-    p->off_units = res.image[pka::kHdrOffUnits];
-    p->off_req = res.image[pka::kHdrOffReq];
-    p->off_merge = res.image[pka::kHdrOffMerge];
-    p->off_idx = res.image[pka::kHdrOffIndices];
-    p->off_sched = res.image[pka::kHdrOffSched];
+    p->int_ws_bytes = int_ws_bytes;
+    p->float_ws_bytes = float_ws_bytes;
     p->staging = nullptr;
-    hipError_t e = hipHostMalloc(&p->staging, need, hipHostMallocDefault);
+    p->staging_bytes = 0;
+    hipError_t e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
     if (e != hipSuccess) {
       delete p;
-      return hip_error("hipHostMalloc(plan staging)", e);
+      return hip_error("hipEventCreateWithFlags(plan upload)", e);
     }
-    std::memcpy(p->staging, res.image.data(), need);
-    e = hipMemcpyAsync(int_ws, p->staging, need, hipMemcpyHostToDevice, stream);
-    if (e != hipSuccess) {
-      (void)hipHostFree(p->staging);
+    st = upload(p, res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, stream);
+    if (st != PKA_OK) {
+      (void)hipEventDestroy(p->uploaded);
+      if (p->staging) (void)hipHostFree(p->staging);
       delete p;
-      return hip_error("hipMemcpyAsync(plan upload)", e);
+      return st;
     }
     if (env_int("PKA_LOG"))
       std::fprintf(stderr, "[pka] plan: %s units=%d merge_groups=%d partial_rows=%d kv_chunk=%d int_ws=%zu float_ws=%zu\n",
@@ -469,8 +496,36 @@ int pka_append_paged_kv(const void* append_k, const void* append_v, const int32_
   return PKA_OK;
 }
 
+int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                    const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages, pka_stream_t stream) {
+  try {
+    if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
+    pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
+                                   plan->num_pages, plan->num_qo_heads, plan->num_kv_heads, plan->head_dim,
+                                   plan->page_size, plan->causal, plan->flags, true);
+    pka::PlanResult res;
+    const int st = plan_or_error(in, &res);
+    if (st != PKA_OK) return st;
+    const size_t need = res.image.size() * sizeof(int32_t);
+    if (plan->int_ws_bytes < need)
+      return set_error(PKA_ERR_WORKSPACE, "int workspace has " + std::to_string(plan->int_ws_bytes) +
+                                              " bytes, needs " + std::to_string(need));
+    if (plan->float_ws_bytes < res.float_ws_bytes)
+      return set_error(PKA_ERR_WORKSPACE, "float workspace has " + std::to_string(plan->float_ws_bytes) +
+                                              " bytes, needs " + std::to_string(res.float_ws_bytes));
+    if ((plan->flags & PKA_GRAPH_STABLE) &&
+        (res.kernel != plan->info.kernel || res.num_workers != plan->info.num_workers))
+      return set_error(PKA_ERR_INVALID_ARG,
+                       "a graph-stable plan cannot switch between prefill and decode batches");
+    return upload(plan, res, batch, (plan->flags & PKA_RAGGED_KV) ? 0 : nnz_pages, stream);
+  } catch (const std::exception& ex) {
+    return set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
+
 void pka_plan_destroy(pka_plan* plan) {
   if (!plan_ok(plan)) return;
+  (void)hipEventDestroy(plan->uploaded);
   if (plan->staging) (void)hipHostFree(plan->staging);
   plan->magic = 0;
   delete plan;

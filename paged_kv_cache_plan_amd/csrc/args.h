@@ -16,12 +16,8 @@ struct AttnArgs {
   const uint16_t* v;
   void* o;                   // bf16 or fp32 [total_q, Hq, D]
   float* lse;                // fp32 [total_q, Hq] or null
-  float* part_o;             // fp32 [num_partial_rows, D]
-  float* part_lse;           // fp32 [num_partial_rows]
-  const int32_t* units;      // [num_units][8]
-  const int32_t* req;        // [batch][8]
-  const int32_t* kv_indices; // [nnz] device copy
-  int32_t* sched;            // prefill: [num_queues][64] queue records with their counters
+  float* part_o;             // float workspace: partial O [rows, D], then partial lse
+  int32_t* ws;               // int workspace: the plan image (sections found via its header)
   int64_t page_stride;       // elements between pages (ragged: between tokens)
   int64_t head_stride;       // elements between KV heads
   int32_t row_stride;        // elements between consecutive slots of a page
@@ -30,16 +26,13 @@ struct AttnArgs {
   int32_t page_size;
   int32_t page_shift;        // log2(page_size) when a power of two, else -1
   int32_t out_fp32;
-  int32_t num_queues;        // prefill: unit queues (worker b serves queue b % num_queues)
   float scale_log2;          // sm_scale * log2(e): logits in base-2 units
 };
 
 // Arguments of the split-KV merge that follows an attention launch.
 struct MergeArgs {
-  const float* part_o;
-  const float* part_lse;
-  const int32_t* groups;     // [num_groups][8]
-  const int32_t* req;
+  const float* part_o;       // float workspace (partial lse found via the image header)
+  const int32_t* ws;         // int workspace: the plan image
   void* o;
   float* lse;
   int32_t num_qo_heads;

@@ -1,8 +1,10 @@
 // Single-token decode attention over a paged (or ragged dense) KV cache, gfx950.
 //
-// One workgroup = one work unit (request r, KV head hk, key range
-// [kv_lo, kv_hi)).  The G query heads that share KV head hk are processed
-// together so each K/V byte is read from HBM once.  The four waves take
+// A work unit is (request r, KV head hk, key range [kv_lo, kv_hi)).  The G
+// query heads that share KV head hk are processed together so each K/V byte
+// is read from HBM once.  The launch is persistent: one workgroup per
+// resident slot takes units, longest first, from one queue and starts
+// loading its next unit while it merges and writes the current one.  The four waves take
 // interleaved 32-key steps of the range and keep independent online-softmax
 // states, merged through LDS at the end (the recursive-attention identity:
 // FlashInfer documentation, "Attention States and Recursive Attention").
@@ -43,7 +45,7 @@ __device__ __forceinline__ int dvt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3
 enum IdMode : int { kRagged = 0, kPagedUniform = 1, kPagedLane = 2 };
 
 template <int D, int MODE>
-__global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
+__global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnArgs a) {
   constexpr bool PAGED = MODE != kRagged;
   constexpr int CPR = D / 8;   // 16-byte chunks per row
   constexpr int DS = D / 32;   // k-steps of the S^T MFMA
@@ -54,31 +56,51 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
   constexpr int SMEM = VT_BYTES > MERGE_BYTES ? VT_BYTES : MERGE_BYTES;
   __shared__ __attribute__((aligned(16))) unsigned char smem[SMEM];
 
+  __shared__ int s_unit[2];
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform
-  const int32_t* unit = a.units + static_cast<int64_t>(blockIdx.x) * 8;
-  const int r = unit[0], hk = unit[1];
-  const int kv_lo = unit[4], kv_hi = unit[5], prow = unit[6];
-  const int32_t* rq = a.req + static_cast<int64_t>(r) * 8;
-  const int qo_begin = rq[0], kv_base = rq[2];
   const int G = a.group, Hq = a.num_qo_heads;
+  const PlanView pv = plan_view(a.ws);
 
   const int col = lane & 15;  // query head within the group (MFMA column)
   const int g4 = lane >> 4;   // 16-lane row
   const bool col_ok = col < G;
 
-  bf16x8 qreg[DS];
-  {
-    const uint16_t* qp = a.q + (static_cast<int64_t>(qo_begin) * Hq + hk * G + (col_ok ? col : 0)) * D + 8 * g4;
-#pragma unroll
-    for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(col_ok ? ld16(qp + 32 * s) : u32x4{0, 0, 0, 0});
-  }
+  int32_t* sched = pv.sched + (blockIdx.x % pv.num_queues) * kSchedWords;
+  const int q_begin = sched[kSchedBegin], q_end = sched[kSchedEnd];
+  auto claim = [&](int slot) {
+    if (tid == 0)
+      s_unit[slot] = q_begin + __hip_atomic_fetch_add(sched + kSchedNext, 1, __ATOMIC_RELAXED,
+                                                      __HIP_MEMORY_SCOPE_AGENT);
+  };
+  // fields of a unit and of its request (wave-uniform)
+  struct Unit { int hk, kv_lo, kv_hi, prow, qo_begin, kv_base; };
+  auto load_unit = [&](int ui) {
+    const int32_t* u = pv.units + static_cast<int64_t>(ui) * 8;
+    Unit x;
+    x.hk = u[1];
+    x.kv_lo = u[4];
+    x.kv_hi = u[5];
+    x.prow = u[6];
+    const int32_t* rq = pv.req + static_cast<int64_t>(u[0]) * 8;
+    x.qo_begin = rq[0];
+    x.kv_base = rq[2];
+    return x;
+  };
 
+  bf16x8 qreg[DS];
   const int ps = a.page_size, pshift = a.page_shift;
-  constexpr bool scalar_ids = MODE == kPagedUniform;
-  const uint16_t* kb_ptr = a.k + hk * a.head_stride;
-  const uint16_t* vb_ptr = a.v + hk * a.head_stride;
+  int hk = 0, kv_hi = 0, kv_base = 0;  // of the unit being loaded
+  const uint16_t* kb_ptr = a.k;
+  const uint16_t* vb_ptr = a.v;
+  auto bind = [&](const Unit& U) {
+    hk = U.hk;
+    kv_hi = U.kv_hi;
+    kv_base = U.kv_base;
+    kb_ptr = a.k + U.hk * a.head_stride;
+    vb_ptr = a.v + U.hk * a.head_stride;
+  };
 
   // V loader: lane handles chunk vc of the 8 keys in slot group vg.
   const int vc = lane % CPR, vg = lane / CPR;
@@ -97,19 +119,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
                 typename std::conditional<MODE == kPagedLane, IdsLane, IdsNone>::type>::type;
   auto fetch_ids = [&](int k0, Ids& id) {
     if constexpr (MODE == kPagedUniform) {
-      id.s[0] = a.kv_indices[kv_base + (k0 >> pshift)];
-      id.s[1] = (k0 + 16 < kv_hi) ? a.kv_indices[kv_base + ((k0 + 16) >> pshift)] : id.s[0];
+      id.s[0] = pv.kv_indices[kv_base + (k0 >> pshift)];
+      id.s[1] = (k0 + 16 < kv_hi) ? pv.kv_indices[kv_base + ((k0 + 16) >> pshift)] : id.s[0];
     } else if constexpr (MODE == kPagedLane) {
       {
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
           const int key = k0 + 16 * kb + col;
-          id.k[kb] = key < kv_hi ? a.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
+          id.k[kb] = key < kv_hi ? pv.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
         }
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const int key = k0 + v_key(j);
-          id.v[j] = (v_lane && key < kv_hi) ? a.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
+          id.v[j] = (v_lane && key < kv_hi) ? pv.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
         }
       }
     }
@@ -149,28 +171,52 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
     }
   };
 
+  // Steps t = wave, wave + 4, ...: page ids two steps ahead, data one ahead.
+  Ids ids_next{};
+  Data cur{}, nxt{};
+  auto start_unit = [&](const Unit& U) {
+    bind(U);
+    const uint16_t* qp = a.q + (static_cast<int64_t>(U.qo_begin) * Hq + U.hk * G + (col_ok ? col : 0)) * D + 8 * g4;
+#pragma unroll
+    for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(col_ok ? ld16(qp + 32 * s) : u32x4{0, 0, 0, 0});
+    const int n = U.kv_hi > U.kv_lo ? (U.kv_hi - U.kv_lo + kTK - 1) / kTK : 0;
+    if (wave < n) {
+      Ids ids0{};
+      fetch_ids(U.kv_lo + wave * kTK, ids0);
+      fetch_data(U.kv_lo + wave * kTK, ids0, cur);
+      if (wave + kWaves < n) fetch_ids(U.kv_lo + (wave + kWaves) * kTK, ids_next);
+    }
+  };
+
+  claim(0);
+  __syncthreads();
+  int ui = __builtin_amdgcn_readfirstlane(s_unit[0]);
+  int slot = 0;
+  Unit U{};
+  if (ui < q_end) {
+    U = load_unit(ui);
+    start_unit(U);
+  }
+  while (ui < q_end) {
+  const int kv_lo = U.kv_lo, prow = U.prow, qo_begin = U.qo_begin;
   f32x4 o[DB];
 #pragma unroll
   for (int b = 0; b < DB; ++b) o[b] = f32x4{};
   float m_run = -INFINITY, l_run = 0.f;
   const float sl2 = a.scale_log2;
 
-  // Steps t = wave, wave + 4, ...: page ids two steps ahead, data one ahead.
   const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kTK - 1) / kTK : 0;
-  Ids ids_next{};
-  Data cur{}, nxt{};
+  // wave 0 claims the next unit at its last step (at once if it has none);
+  // the first merge barrier publishes the claim
+  if (wave == 0 && wave >= n_tiles) claim(slot ^ 1);
   int t = wave;
-  if (t < n_tiles) {
-    Ids ids0{};
-    fetch_ids(kv_lo + t * kTK, ids0);
-    fetch_data(kv_lo + t * kTK, ids0, cur);
-    if (t + kWaves < n_tiles) fetch_ids(kv_lo + (t + kWaves) * kTK, ids_next);
-  }
   for (; t < n_tiles; t += kWaves) {
     const int k0 = kv_lo + t * kTK;
     if (t + kWaves < n_tiles) {
       fetch_data(k0 + kWaves * kTK, ids_next, nxt);
       if (t + 2 * kWaves < n_tiles) fetch_ids(k0 + 2 * kWaves * kTK, ids_next);
+    } else if (wave == 0) {
+      claim(slot ^ 1);
     }
 
     f32x4 s[2];
@@ -250,7 +296,18 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
 
   // ---- merge the four waves' states -------------------------------------
   float l_tot = xor32_sum(xor16_sum(l_run));
-  __syncthreads();  // every wave is done with its V^T tile
+  __syncthreads();  // every wave is done with its V^T tile; publishes the claim
+  // the next unit's Q, page ids and first K/V step load during this merge;
+  // the s_unit slot claimed now was last read one unit ago, before barriers
+  // every thread has since passed
+  const int un = __builtin_amdgcn_readfirstlane(s_unit[slot ^ 1]);
+  const int c_hk = hk;
+  if (un < q_end) {
+    U = load_unit(un);
+    start_unit(U);
+  }
+  ui = un;
+  slot ^= 1;
   float* wo = reinterpret_cast<float*>(smem);            // [wave][16][D]
   float* wm = wo + kWaves * 16 * D;                       // [wave][16]
   float* wl = wm + kWaves * 16;                           // [wave][16]
@@ -282,7 +339,7 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
     const float val = seen ? acc / L : 0.f;
     const float lse = seen ? M + __log2f(L) : -INFINITY;
     if (prow < 0) {
-      const int64_t orow = static_cast<int64_t>(qo_begin) * Hq + hk * G + c;
+      const int64_t orow = static_cast<int64_t>(qo_begin) * Hq + c_hk * G + c;
       if (a.out_fp32)
         static_cast<float*>(a.o)[orow * D + d] = val;
       else
@@ -290,7 +347,19 @@ __global__ __launch_bounds__(kThreads) void decode_kernel(AttnArgs a) {
       if (a.lse && d == 0) a.lse[orow] = lse;
     } else {
       a.part_o[static_cast<int64_t>(prow + c) * D + d] = val;
-      if (d == 0) a.part_lse[prow + c] = lse;
+      if (d == 0) a.part_o[pv.partial_lse + prow + c] = lse;
+    }
+  }
+  __syncthreads();  // the next unit's V^T tiles reuse the merge buffers
+  }
+
+  // The last worker of the queue to get here resets its counters for the
+  // next run; acq_rel orders every worker's final take before the reset.
+  if (tid == 0) {
+    const int done = __hip_atomic_fetch_add(sched + kSchedDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == sched[kSchedWorkers] - 1) {
+      __hip_atomic_store(sched + kSchedNext, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(sched + kSchedDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }

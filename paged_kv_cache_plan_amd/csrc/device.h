@@ -6,6 +6,8 @@
 
 #include <cstdint>
 
+#include "planner.h"
+
 namespace pka {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
@@ -55,5 +57,31 @@ __device__ __forceinline__ uint32_t pack_hi16(uint32_t a, uint32_t b) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+// The sections of a plan image in device memory, read from its header
+// (wave-uniform scalar loads), so that kernel arguments do not depend on the
+// batch that was planned.
+struct PlanView {
+  const int32_t* units;
+  const int32_t* req;
+  const int32_t* kv_indices;
+  const int32_t* merge;
+  int32_t* sched;
+  int32_t num_queues;
+  int32_t num_merge;
+  int32_t partial_lse;  // float index of the partial lse in the float workspace
+};
+__device__ __forceinline__ PlanView plan_view(const int32_t* ws) {
+  PlanView v;
+  v.units = ws + ws[kHdrOffUnits];
+  v.req = ws + ws[kHdrOffReq];
+  v.kv_indices = ws + ws[kHdrOffIndices];
+  v.merge = ws + ws[kHdrOffMerge];
+  v.sched = const_cast<int32_t*>(ws) + ws[kHdrOffSched];
+  v.num_queues = ws[kHdrNumQueues];
+  v.num_merge = ws[kHdrNumMerge];
+  v.partial_lse = ws[kHdrPartialLse];
+  return v;
+}
 
 }  // namespace pka

@@ -30,25 +30,30 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v, bool fp3
   }
 }
 
-// One workgroup per split group: rows [row0, row1) of (request, kv head).
+// Split groups, one per workgroup, grid-stride: rows [row0, row1) of
+// (request, kv head).  The group list and its length come from the plan
+// image, so the launch does not depend on the batch.
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_split_kernel(MergeArgs a) {
   constexpr int C4 = D / 4;
-  const int32_t* g = a.groups + static_cast<int64_t>(blockIdx.x) * 8;
+  const PlanView pv = plan_view(a.ws);
+  const float* part_lse = a.part_o + pv.partial_lse;
+  for (int gi = blockIdx.x; gi < pv.num_merge; gi += gridDim.x) {
+  const int32_t* g = pv.merge + static_cast<int64_t>(gi) * 8;
   const int r = g[0], hk = g[1], row0 = g[2], row1 = g[3], pbase = g[4], S = g[5];
   const int nrows = row1 - row0;
-  const int qo_begin = a.req[static_cast<int64_t>(r) * 8];
+  const int qo_begin = pv.req[static_cast<int64_t>(r) * 8];
   const int G = a.group, Hq = a.num_qo_heads;
   for (int it = threadIdx.x; it < nrows * C4; it += kThreads) {
     const int row = it / C4, c4 = it - row * C4;
     float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, a.part_lse[pbase + s * nrows + row]);
+    for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[pbase + s * nrows + row]);
     float W = 0.f;
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
     if (M != -INFINITY) {
       for (int s = 0; s < S; ++s) {
         const int64_t prow = pbase + s * nrows + row;
-        const float w = fast_exp2(a.part_lse[prow] - M);
+        const float w = fast_exp2(part_lse[prow] - M);
         if (w > 0.f) {
           W += w;
           acc += w * *reinterpret_cast<const f32x4*>(a.part_o + prow * D + 4 * c4);
@@ -62,6 +67,7 @@ __global__ __launch_bounds__(kThreads) void merge_split_kernel(MergeArgs a) {
     const int64_t orow = static_cast<int64_t>(qo_begin + tok) * Hq + hk * G + (p - tok * G);
     store4(a.o, orow * D + 4 * c4, acc * inv, a.out_fp32 != 0);
     if (a.lse && c4 == 0) a.lse[orow] = seen ? M + __log2f(W) : -INFINITY;
+  }
   }
 }
 

@@ -197,13 +197,16 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
     if (a.cost != b.cost) return a.cost > b.cost;
     return a.seq < b.seq;
   };
-  // Queues (prefill): queue_begin[q] .. queue_begin[q + 1] index the unit array.
+  // Queues: queue_begin[q] .. queue_begin[q + 1] index the unit array.
+  const bool fixed = (in.flags & kFlagGraphStable) != 0;
   std::vector<int32_t> queue_begin{0};
   if (decode) {
-    // Longest-first order: the hardware hands out workgroups roughly in index
-    // order, so big units start first and small ones fill the tail.
+    // One queue, longest first: big units start first and small ones fill
+    // the tail.  Decode reads each K/V byte once, so there is no L2 reuse to
+    // keep on one XCD.
     std::stable_sort(units.begin(), units.end(), longest_first);
-  } else if (in.num_xcds <= 1 || units.size() <= static_cast<size_t>(in.num_xcds)) {
+    queue_begin.push_back(static_cast<int32_t>(units.size()));
+  } else if (in.num_xcds <= 1 || (!fixed && units.size() <= static_cast<size_t>(in.num_xcds))) {
     std::stable_sort(units.begin(), units.end(), longest_first);
     queue_begin.push_back(static_cast<int32_t>(units.size()));
   } else {
@@ -255,16 +258,17 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
     }
     units.swap(out);
   }
+  // Workers: at most one per resident slot.  With kFlagGraphStable the
+  // count does not depend on the batch (queues may be empty).
   const int32_t n_queues = static_cast<int32_t>(queue_begin.size()) - 1;
-  int32_t n_workers = static_cast<int32_t>(units.size());
-  int32_t workers_per_queue = 0;
-  if (n_queues > 0) {
-    int64_t longest = 0;
-    for (int q = 0; q < n_queues; ++q) longest = std::max<int64_t>(longest, queue_begin[q + 1] - queue_begin[q]);
-    const int64_t slots = int64_t(std::max(1, in.num_cus)) * prefill_wg_per_cu(in.head_dim);
-    workers_per_queue = static_cast<int32_t>(std::max<int64_t>(1, std::min<int64_t>(longest, slots / n_queues)));
-    n_workers = n_queues * workers_per_queue;
-  }
+  int64_t longest = 0;
+  for (int q = 0; q < n_queues; ++q) longest = std::max<int64_t>(longest, queue_begin[q + 1] - queue_begin[q]);
+  const int64_t slots =
+      int64_t(std::max(1, in.num_cus)) * (decode ? kDecodeWgPerCu : prefill_wg_per_cu(in.head_dim));
+  const int64_t per_queue_max = std::max<int64_t>(1, slots / n_queues);
+  const int32_t workers_per_queue =
+      static_cast<int32_t>(fixed ? per_queue_max : std::max<int64_t>(1, std::min<int64_t>(longest, per_queue_max)));
+  const int32_t n_workers = n_queues * workers_per_queue;
 
   // Assemble the image.
   const int32_t n_units = static_cast<int32_t>(units.size());
@@ -329,6 +333,9 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   out->total_kv = total_kv;
   const size_t o_bytes = static_cast<size_t>(partial_rows) * in.head_dim * sizeof(float);
   out->partial_lse_offset = (o_bytes + 255) / 256 * 256;
+  if (out->partial_lse_offset / sizeof(float) >= (size_t(1) << 31))
+    return fail(err, kUnsupported, "too many partial rows");
+  out->image[kHdrPartialLse] = static_cast<int32_t>(out->partial_lse_offset / sizeof(float));
   out->float_ws_bytes = out->partial_lse_offset +
                         (static_cast<size_t>(partial_rows) * sizeof(float) + 255) / 256 * 256;
   if (out->float_ws_bytes == 0) out->float_ws_bytes = 256;

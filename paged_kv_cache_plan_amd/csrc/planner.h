@@ -35,9 +35,10 @@ enum HeaderField : int {
   kHdrBlockRows,
   kHdrKvChunk,
   kHdrFlags,
-  kHdrOffSched,     // prefill: per-queue scheduling records (see SchedField)
-  kHdrNumQueues,    // prefill: number of unit queues (0 for decode)
-  kHdrNumWorkers,   // workgroups to launch
+  kHdrOffSched,     // per-queue scheduling records (see SchedField)
+  kHdrNumQueues,    // number of unit queues
+  kHdrNumWorkers,   // workgroups of the attention launch
+  kHdrPartialLse,   // float index of the partial lse section in the float workspace
   kHdrWords = 32
 };
 constexpr int32_t kMagic = 0x31414b50;  // "PKA1"
@@ -78,8 +79,11 @@ enum MergeField : int {
   kMergeWords = 8
 };
 
-// Prefill runs as a persistent launch: kHdrNumWorkers workgroups, worker b
-// serving queue b % kHdrNumQueues.  Queue q owns units [begin, end) of the
+// Attention runs as a persistent launch: kHdrNumWorkers workgroups, worker b
+// serving queue b % kHdrNumQueues (prefill: one queue per XCD; decode: one).
+// The kernels find every section and count through this header, so a launch
+// whose grid does not depend on the batch can be replayed after the image
+// has been replaced by another batch's.  Queue q owns units [begin, end) of the
 // unit array; a worker takes the next unit with an atomic increment of the
 // queue's counter.  The last worker of a queue to finish sets both counters
 // back to zero, so the next run of the plan starts from a clean state without
@@ -100,11 +104,14 @@ enum Kernel : int { kPrefill = 0, kDecode = 1 };
 constexpr int kPrefillBlockKeys = 64;   // keys per prefill KV tile
 constexpr int kDecodeTileKeys = 32;     // keys per decode wave step
 constexpr int kDecodeMaxGroup = 16;     // decode kernel holds up to 16 query heads per KV head
+constexpr int kDecodeWgPerCu = 2;       // resident decode workgroups per CU (persistent launch)
+constexpr int kMergeGrid = 1024;        // split-merge workgroups of a batch-independent launch
 constexpr int kQueueWindow = 2;         // prefill queue: groups per longest-first window
 
 constexpr uint32_t kFlagDisableSplit = 0x1u;
 constexpr uint32_t kFlagOutFp32 = 0x2u;
 constexpr uint32_t kFlagRagged = 0x4u;
+constexpr uint32_t kFlagGraphStable = 0x8u;  // launch shapes that do not depend on the batch
 
 enum Status : int { kOk = 0, kInvalid = 1, kUnsupported = 2, kWorkspace = 3, kHip = 4 };
 

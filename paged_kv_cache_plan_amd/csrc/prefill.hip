@@ -71,8 +71,8 @@ struct UnitInfo {
   int qo_begin, qo_len, kv_base, kv_len;
 };
 
-__device__ __forceinline__ UnitInfo load_unit(const AttnArgs& a, int ui) {
-  const int32_t* u = a.units + static_cast<int64_t>(ui) * 8;
+__device__ __forceinline__ UnitInfo load_unit(const PlanView& pv, int ui) {
+  const int32_t* u = pv.units + static_cast<int64_t>(ui) * 8;
   UnitInfo x;
   x.r = u[0];
   x.hk = u[1];
@@ -81,7 +81,7 @@ __device__ __forceinline__ UnitInfo load_unit(const AttnArgs& a, int ui) {
   x.kv_lo = u[4];
   x.kv_hi = u[5];
   x.prow = u[6];
-  const int32_t* rq = a.req + static_cast<int64_t>(x.r) * 8;
+  const int32_t* rq = pv.req + static_cast<int64_t>(x.r) * 8;
   x.qo_begin = rq[0];
   x.qo_len = rq[1];
   x.kv_base = rq[2];
@@ -127,7 +127,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
   // Persistent: take units from this worker's queue until it runs dry.  The
   // next unit is claimed during the current unit's last tile, and its Q and
   // first K/V tile are in flight while the current unit writes its output.
-  int32_t* sched = a.sched + (blockIdx.x % a.num_queues) * kSchedWords;
+  const PlanView pv = plan_view(a.ws);
+  int32_t* sched = pv.sched + (blockIdx.x % pv.num_queues) * kSchedWords;
   const int q_begin = sched[kSchedBegin], q_end = sched[kSchedEnd];
   auto claim = [&](int slot) {
     if (tid == 0)
@@ -161,7 +162,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
   auto slot_of = [&](int key) { return pow2 ? (key & (ps - 1)) : (key - (key / ps) * ps); };
   auto fetch_ids = [&](const UnitInfo& U, int k0, int* ids) {
     if constexpr (PAGED) {
-      const int32_t* idx = a.kv_indices + U.kv_base;
+      const int32_t* idx = pv.kv_indices + U.kv_base;
       const int key0 = k0 + KPT * lj;
       if constexpr (one_page) {
         ids[0] = key0 < U.kv_hi ? idx[key0 >> pshift] : 0;
@@ -272,7 +273,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
   int slot = 0;
   UnitInfo U{};
   if (ui < q_end) {
-    U = load_unit(a, ui);
+    U = load_unit(pv, ui);
     start_unit(U);
   }
 
@@ -403,7 +404,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
     const int un = __builtin_amdgcn_readfirstlane(s_unit[slot ^ 1]);
     const UnitInfo Uc = U;
     if (un < q_end) {
-      U = load_unit(a, un);
+      U = load_unit(pv, un);
       start_unit(U);
     }
     ui = un;
@@ -457,7 +458,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
               *reinterpret_cast<f32x4*>(op + d0) =
                   f32x4{o[b][4 * g] * inv, o[b][4 * g + 1] * inv, o[b][4 * g + 2] * inv, o[b][4 * g + 3] * inv};
             }
-          if (hf == 0) a.part_lse[prow_i] = lse;
+          if (hf == 0) a.part_o[pv.partial_lse + prow_i] = lse;
         }
       }
     }

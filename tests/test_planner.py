@@ -107,12 +107,12 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             units.append(([r, hk, r0, r1, lo, up, base + s_ * nrows if n > 1 else -1, 0],
                           (up - lo) * nrows + 1, len(units)))
     key = lambda u: (-u[1], u[2])
-    bounds = [0]  # prefill queue q holds units bounds[q] .. bounds[q + 1]
-    if decode or len(units) <= NUM_XCDS:
+    fixed = bool(flags & pka.PKA_GRAPH_STABLE)
+    bounds = [0]  # queue q holds units bounds[q] .. bounds[q + 1]
+    if decode or (len(units) <= NUM_XCDS and not fixed):
         units.sort(key=key)
         order = [u[0] for u in units]
-        if not decode:
-            bounds.append(len(order))
+        bounds.append(len(order))
     else:
         grps, i = [], 0
         while i < len(units):
@@ -138,12 +138,10 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             order += q
             bounds.append(len(order))
     nq = len(bounds) - 1
-    workers, per_queue = len(order), 0
-    if nq:
-        longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
-        slots = NUM_CUS * wg_per_cu(D)
-        per_queue = max(1, min(longest, slots // nq))
-        workers = nq * per_queue
+    longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
+    slots = NUM_CUS * (2 if decode else wg_per_cu(D))
+    per_queue = max(1, slots // nq) if fixed else max(1, min(longest, max(1, slots // nq)))
+    workers = nq * per_queue
     align = lambda w: _cdiv(w, 64) * 64
     nnz = 0 if ragged else kv_indptr[B]
     off_units = 64
@@ -153,8 +151,10 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     off_idx = off_sched + align(nq * 64)
     total = off_idx + align(max(nnz, 1))
     img = [0] * total
+    part_lse = _cdiv(partial * D * 4, 256) * 256 // 4
     hdr = [0x31414b50, 1 if decode else 0, len(order), len(merge), B, nnz, off_units, off_req,
-           off_merge, off_idx, partial, rows_per, chunk if any_split else 0, flags, off_sched, nq, workers]
+           off_merge, off_idx, partial, rows_per, chunk if any_split else 0, flags, off_sched, nq, workers,
+           part_lse]
     img[:len(hdr)] = hdr
     for q in range(nq):  # counters (words 0, 1) start at zero
         img[off_sched + 64 * q + 32: off_sched + 64 * q + 35] = [bounds[q], bounds[q + 1], per_queue]
@@ -316,11 +316,35 @@ def test_prefill_queues(name, kw):
             assert home.setdefault((u[0], u[1]), q) == q
 
 
-def test_decode_has_no_queues():
+def test_decode_single_queue():
+    """Decode: one queue over every unit, longest first; at most two workers per CU."""
     w = W.batch_decode(batch=20)
     img, info = _image(w)
     assert info["kernel"] == pka.PKA_KERNEL_DECODE
-    assert info["num_queues"] == 0 and info["num_workers"] == info["num_units"]
+    h = img[:32].tolist()
+    off_sched, nq, workers = h[14], h[15], h[16]
+    assert nq == 1 and info["num_queues"] == 1
+    rec = img[off_sched: off_sched + 64].tolist()
+    assert rec[0] == 0 and rec[1] == 0 and rec[32] == 0 and rec[33] == info["num_units"]
+    assert workers == rec[34] == min(info["num_units"], 2 * NUM_CUS) == info["num_workers"]
+
+
+@pytest.mark.parametrize("name,kw", [("tiny", {}), ("gqa_append", dict(batch=3, prefix_range=(10, 90),
+                                                                       chunk_range=(1, 20))),
+                                     ("batch_decode", dict(batch=5))])
+def test_graph_stable_launch_shape(name, kw):
+    """With PKA_GRAPH_STABLE the queue count and worker count depend only on
+    the kernel kind and head_dim, never on the batch."""
+    w = W.make(name, **kw)
+    img, info = _image(w, flags=pka.PKA_GRAPH_STABLE)
+    want = restate_plan(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
+                        w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size,
+                        w.causal, pka.PKA_GRAPH_STABLE, D=w.head_dim)
+    assert img.tolist() == want
+    if info["kernel"] == pka.PKA_KERNEL_DECODE:
+        assert info["num_queues"] == 1 and info["num_workers"] == 2 * NUM_CUS
+    else:
+        assert info["num_queues"] == NUM_XCDS and info["num_workers"] == NUM_CUS * wg_per_cu(w.head_dim)
 
 
 def test_visible_pairs_brute():
