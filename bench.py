@@ -178,6 +178,81 @@ def bench_append(w, dev, steps, warmup, copies=4, pools=2):
     # (the caller drops the workload afterwards; the copies go with this frame)
 
 
+def _sub_batch(w, rs):
+    """Page table and row indices of requests rs of w, as a batch of their own."""
+    qo, kv, idx, last, rows = [0], [0], [], [], []
+    for r in rs:
+        a, b = int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])
+        rows += list(range(a, b))
+        qo.append(qo[-1] + b - a)
+        pa, pb = int(w.kv_indptr[r]), int(w.kv_indptr[r + 1])
+        kv.append(kv[-1] + pb - pa)
+        idx += w.kv_indices[pa:pb].tolist()
+        last.append(int(w.kv_last_page_len[r]))
+    return qo, kv, idx, last, rows
+
+
+def bench_mixed(w, dev, steps, warmup, copies=2):
+    """One chunked-prefill serving step (prefill chunks and decode requests in
+    one batch), three ways, each timed with HIP events on the caller's stream:
+    (a) PKA_MIXED_BATCH: the prefill and decode kernels side by side on a
+    split of the compute units; (b) one ordinary plan, whose prefill kernel
+    takes every row; (c) the prefill requests, then the decode requests, as
+    two plans run one after the other."""
+    import torch
+    import paged_kv_cache_plan_amd as pka
+    mk = lambda qo, kv, idx, last, **kw: pka.Plan(qo, kv, idx, last, w.num_qo_heads, w.num_kv_heads, w.head_dim,
+                                                  w.page_size, causal=w.causal, sm_scale=w.sm_scale,
+                                                  num_pages=w.num_pages, device=dev, **kw)
+    full = (w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len)
+    t0 = time.perf_counter()
+    plan_mixed = mk(*full, mixed=True)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    plan_whole = mk(*full)
+    pre = [r for r in range(w.batch) if w.qo_lens[r] > 1]
+    dec = [r for r in range(w.batch) if w.qo_lens[r] == 1]
+    sp, sd = _sub_batch(w, pre), _sub_batch(w, dec)
+    plan_p, plan_d = mk(*sp[:4]), mk(*sd[:4])
+    qs = [w.q] + [w.q.clone() for _ in range(copies - 1)]
+    pools = [w.paged_kv] + [w.paged_kv.clone() for _ in range(copies - 1)]
+    q_p = [q[sp[4]] for q in qs]
+    q_d = [q[sd[4]] for q in qs]
+    H, D = w.num_qo_heads, w.head_dim
+    o = torch.empty((w.total_q, H, D), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.total_q, H), dtype=torch.float32, device=dev)
+    o_p, l_p = o[:len(sp[4])], lse[:len(sp[4])]
+    o_d, l_d = o[len(sp[4]):], lse[len(sp[4]):]
+
+    def run_mixed(i):
+        plan_mixed.run(qs[i % copies], pools[i % copies], o, lse)
+
+    def run_whole(i):
+        plan_whole.run(qs[i % copies], pools[i % copies], o, lse)
+
+    def run_seq(i):
+        plan_p.run(q_p[i % copies], pools[i % copies], o_p, l_p)
+        plan_d.run(q_d[i % copies], pools[i % copies], o_d, l_d)
+
+    res = {"kernel": "mixed", "plan_ms": plan_ms, "requests_prefill": len(pre), "requests_decode": len(dec),
+           "prefill_cus": plan_mixed.info["prefill_cus"], "decode_cus": plan_mixed.info["decode_cus"]}
+    for name, fn in (("mixed", run_mixed), ("single_launch", run_whole), ("sequential", run_seq)):
+        _, per = time_launches(fn, steps, warmup)
+        res[f"{name}_ms_avg"] = sum(per) / len(per)
+        res[f"{name}_ms_median"] = sorted(per)[len(per) // 2]
+    for p in (plan_mixed, plan_whole, plan_p, plan_d):
+        p.close()
+    flop = 4.0 * D * H * pka.visible_pairs([w.qo_lens[r] for r in pre], [w.kv_lens[r] for r in pre], w.causal)
+    kv_bytes = 4.0 * w.num_kv_heads * D * sum(w.kv_lens[r] for r in dec)
+    t = res["mixed_ms_avg"] * 1e-3
+    res.update({"prefill_flops": flop, "decode_kv_bytes": kv_bytes,
+                "speedup_vs_sequential": res["sequential_ms_avg"] / res["mixed_ms_avg"],
+                "speedup_vs_single_launch": res["single_launch_ms_avg"] / res["mixed_ms_avg"],
+                "ms_per_step": res["mixed_ms_avg"]})
+    del qs, pools, q_p, q_d, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The CPU fp64 oracle, as it stands, on a bounded sample of the headline
     workload (the same inputs the GPU was timed on, copied to the host):
@@ -220,7 +295,7 @@ def main():
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--only", default=None,
-                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5, append (profiling runs)")
+                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5, append, mixed (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -286,6 +361,12 @@ def main():
         print(f"# append: {results['chunk_append']}", file=sys.stderr, flush=True)
         del wa
     torch.cuda.empty_cache()
+    if want("mixed"):
+        wm = W.mixed_batch(device=dev)
+        results["mixed_batch"] = bench_mixed(wm, dev, args.steps, args.warmup)
+        print(f"# mixed: {results['mixed_batch']}", file=sys.stderr, flush=True)
+        del wm
+        torch.cuda.empty_cache()
 
     if sel is not None:
         print(json.dumps({"only": sel, "results": results}))

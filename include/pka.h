@@ -73,13 +73,25 @@ enum {
                                      pka_plan_update has planned another batch into the same
                                      workspaces (FlashInfer 0.2 release blog, "CUDAGraph
                                      compatibility for variable-length inputs")              */
+#define PKA_MIXED_BATCH 0x10u     /* a batch with both prefill requests (qo_len > 1) and decode
+                                     requests (qo_len == 1) runs as two persistent launches side
+                                     by side: the prefill kernel on part of the compute units and
+                                     the decode kernel, on a stream the plan owns, on the rest;
+                                     the caller's stream waits for both.  The split comes from
+                                     the algorithmic work of each side.  (Prefill and decode
+                                     co-scheduled for chunked prefill, and attention on a subset
+                                     of the compute units: "[Roadmap] FlashInfer v0.2 to v0.3",
+                                     milestones "POD-Attention Integration" and "Nanoflow
+                                     Parallelism"; FlashInfer documentation contents,
+                                     "flashinfer.pod".)  A batch of one kind plans as without the
+                                     flag.  Not with PKA_GRAPH_STABLE; not for pka_debug_gather. */
 
 /* Which attention kernel a plan launches. */
-enum { PKA_KERNEL_PREFILL = 0, PKA_KERNEL_DECODE = 1 };
+enum { PKA_KERNEL_PREFILL = 0, PKA_KERNEL_DECODE = 1, PKA_KERNEL_MIXED = 2 };
 
 /* Summary of a plan (all counts are exact for the planned batch). */
 typedef struct pka_plan_info {
-  int32_t kernel;           /* PKA_KERNEL_PREFILL or PKA_KERNEL_DECODE                    */
+  int32_t kernel;           /* PKA_KERNEL_PREFILL, PKA_KERNEL_DECODE or PKA_KERNEL_MIXED  */
   int32_t num_units;        /* work units (decode: one workgroup each)                      */
   int32_t num_merge_groups; /* split (request, kv head, row block) groups merged afterwards */
   int32_t num_partial_rows; /* fp32 partial-state rows held in the float workspace          */
@@ -93,7 +105,9 @@ typedef struct pka_plan_info {
   int64_t float_ws_bytes;   /* bytes of float workspace the runs need                       */
   int32_t num_workers;      /* workgroups of the attention launch (prefill: persistent,
                                each takes units from a queue until it is empty)            */
-  int32_t num_queues;       /* prefill unit queues, one per XCD; 0 for decode                */
+  int32_t num_queues;       /* unit queues: one per XCD for prefill, one for decode          */
+  int32_t prefill_cus;      /* mixed batch: compute units the prefill launch is sized for    */
+  int32_t decode_cus;       /* mixed batch: compute units the decode launch is sized for     */
 } pka_plan_info;
 
 /* Message for the last failed call on this thread ("" if none). */

@@ -30,9 +30,11 @@ PKA_DISABLE_SPLIT_KV = 0x1
 PKA_OUT_FP32 = 0x2
 PKA_RAGGED_KV = 0x4
 PKA_GRAPH_STABLE = 0x8
+PKA_MIXED_BATCH = 0x10
 
 PKA_KERNEL_PREFILL = 0
 PKA_KERNEL_DECODE = 1
+PKA_KERNEL_MIXED = 2
 
 EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka_plan_get_info",
             "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
@@ -48,7 +50,8 @@ class PlanInfo(ctypes.Structure):
                 ("batch", ctypes.c_int32), ("nnz_pages", ctypes.c_int32),
                 ("total_q", ctypes.c_int64), ("total_kv", ctypes.c_int64),
                 ("int_ws_bytes", ctypes.c_int64), ("float_ws_bytes", ctypes.c_int64),
-                ("num_workers", ctypes.c_int32), ("num_queues", ctypes.c_int32)]
+                ("num_workers", ctypes.c_int32), ("num_queues", ctypes.c_int32),
+                ("prefill_cus", ctypes.c_int32), ("decode_cus", ctypes.c_int32)]
 
     def as_dict(self):
         return {k: getattr(self, k) for k, _ in self._fields_}
@@ -193,19 +196,22 @@ class Plan:
     the same launches for every batch, so a captured run can be replayed
     after ``update``; size their workspaces for the largest batch with
     ``int_ws_bytes`` / ``float_ws_bytes`` (at least what this batch needs is
-    allocated).
+    allocated).  ``mixed`` plans a batch of prefill and decode requests as
+    two concurrent launches over a split of the compute units.
     """
 
     def __init__(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads,
                  num_kv_heads, head_dim, page_size=1, causal=True, sm_scale=None,
                  num_pages=None, ragged=False, disable_split_kv=False, out_fp32=False,
-                 device=None, stream=None, graph_stable=False, int_ws_bytes=0, float_ws_bytes=0):
+                 device=None, stream=None, graph_stable=False, int_ws_bytes=0, float_ws_bytes=0,
+                 mixed=False):
         import torch
         L = load_library()
         self._lib = L
         self._handle = ctypes.c_void_p()
         flags = (PKA_RAGGED_KV if ragged else 0) | (PKA_DISABLE_SPLIT_KV if disable_split_kv else 0) \
-            | (PKA_OUT_FP32 if out_fp32 else 0) | (PKA_GRAPH_STABLE if graph_stable else 0)
+            | (PKA_OUT_FP32 if out_fp32 else 0) | (PKA_GRAPH_STABLE if graph_stable else 0) \
+            | (PKA_MIXED_BATCH if mixed else 0)
         self.flags = flags
         self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
         self.page_size = page_size

@@ -33,12 +33,21 @@ int hip_error(const char* what, hipError_t e) {
 }
 
 constexpr uint32_t kPlanMagic = 0x4e4c5050u;  // "PPLN"
-constexpr uint32_t kKnownFlags = PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV | PKA_GRAPH_STABLE;
+constexpr uint32_t kKnownFlags =
+    PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV | PKA_GRAPH_STABLE | PKA_MIXED_BATCH;
 
 int env_int(const char* name) {
   const char* s = std::getenv(name);
   return s ? std::atoi(s) : 0;
 }
+
+// One attention launch of a plan (and its split merge): a mixed batch has
+// two, the prefill one first.
+struct PartLaunch {
+  int32_t kernel, num_workers, num_merge;
+  int32_t off_words;  // its image inside the int workspace
+  size_t float_off;   // its partial states inside the float workspace (bytes)
+};
 
 }  // namespace
 
@@ -56,6 +65,12 @@ struct pka_plan {
   void* staging;        // pinned copy of the image, read by the enqueued copy
   size_t staging_bytes;
   hipEvent_t uploaded;  // recorded after the image copy
+  int32_t num_parts;
+  PartLaunch parts[2];
+  // PKA_MIXED_BATCH: the decode launch runs on `side`, forked from and joined
+  // back into the caller's stream with the two events.
+  hipStream_t side;
+  hipEvent_t fork, join;
 };
 
 namespace {
@@ -80,6 +95,7 @@ pka::PlanInput make_input(const int32_t* qo_indptr, const int32_t* kv_indptr, co
   in.flags = flags;
   in.check_indices = check_indices;
   in.kv_chunk_override = env_int("PKA_KV_CHUNK");
+  in.prefill_cus_override = env_int("PKA_PREFILL_CUS");
   return in;
 }
 
@@ -100,12 +116,43 @@ void fill_info(const pka::PlanResult& res, int32_t batch, int32_t nnz, pka_plan_
   info->num_queues = res.num_queues;
 }
 
-int plan_or_error(const pka::PlanInput& in, pka::PlanResult* res) {
+// The whole plan of a batch (one image, or a mixed batch's two).
+struct Planned {
+  pka::MixedPlan mp;
+  const std::vector<int32_t>& image() const { return mp.mixed ? mp.image : mp.single.image; }
+  size_t float_ws_bytes() const { return mp.mixed ? mp.float_ws_bytes : mp.single.float_ws_bytes; }
+};
+
+int plan_or_error(const pka::PlanInput& in, Planned* res) {
   if (in.flags & ~kKnownFlags) return set_error(PKA_ERR_INVALID_ARG, "unknown flag bits");
   std::string err;
-  const int st = pka::build_plan(in, res, &err);
+  const int st = pka::build_mixed_plan(in, &res->mp, &err);
   if (st != pka::kOk) return set_error(st, err);
   return PKA_OK;
+}
+
+void fill_plan_info(const Planned& pl, int32_t batch, int32_t nnz, pka_plan_info* info) {
+  const pka::MixedPlan& mp = pl.mp;
+  if (!mp.mixed) {
+    fill_info(mp.single, batch, nnz, info);
+    info->prefill_cus = info->decode_cus = 0;
+    return;
+  }
+  fill_info(mp.single, batch, nnz, info);  // totals of the whole batch
+  const pka::PlanResult& a = mp.prefill;
+  const pka::PlanResult& b = mp.decode;
+  info->kernel = PKA_KERNEL_MIXED;
+  info->num_units = a.num_units + b.num_units;
+  info->num_merge_groups = a.num_merge + b.num_merge;
+  info->num_partial_rows = a.num_partial_rows + b.num_partial_rows;
+  info->block_rows = a.block_rows;
+  info->kv_chunk = b.kv_chunk;
+  info->int_ws_bytes = static_cast<int64_t>(mp.image.size() * sizeof(int32_t));
+  info->float_ws_bytes = static_cast<int64_t>(mp.float_ws_bytes);
+  info->num_workers = a.num_workers + b.num_workers;
+  info->num_queues = a.num_queues + b.num_queues;
+  info->prefill_cus = mp.prefill_cus;
+  info->decode_cus = mp.decode_cus;
 }
 
 bool plan_ok(const pka_plan* p) { return p && p->magic == kPlanMagic; }
@@ -113,8 +160,9 @@ bool plan_ok(const pka_plan* p) { return p && p->magic == kPlanMagic; }
 // Copy a planned image into the plan's pinned staging and enqueue its upload
 // to the int workspace; the staging is reused once the previous upload has
 // completed (host waits on that copy only, never on kernels).
-int upload(pka_plan* p, const pka::PlanResult& res, int32_t batch, int32_t nnz, hipStream_t stream) {
-  const size_t need = res.image.size() * sizeof(int32_t);
+int upload(pka_plan* p, const Planned& pl, int32_t batch, int32_t nnz, hipStream_t stream) {
+  const std::vector<int32_t>& image = pl.image();
+  const size_t need = image.size() * sizeof(int32_t);
   if (p->staging) {
     const hipError_t w = hipEventSynchronize(p->uploaded);
     if (w != hipSuccess) return hip_error("hipEventSynchronize(previous plan upload)", w);
@@ -127,18 +175,29 @@ int upload(pka_plan* p, const pka::PlanResult& res, int32_t batch, int32_t nnz, 
     if (a != hipSuccess) return hip_error("hipHostMalloc(plan staging)", a);
     p->staging_bytes = need;
   }
-  std::memcpy(p->staging, res.image.data(), need);
+  std::memcpy(p->staging, image.data(), need);
   hipError_t e = hipMemcpyAsync(p->int_ws, p->staging, need, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_error("hipMemcpyAsync(plan upload)", e);
   e = hipEventRecord(p->uploaded, stream);
   if (e != hipSuccess) return hip_error("hipEventRecord(plan upload)", e);
-  fill_info(res, batch, nnz, &p->info);
+  fill_plan_info(pl, batch, nnz, &p->info);
+  const pka::PlanResult& res = pl.mp.single;
   p->partial_lse_offset = res.partial_lse_offset;
   p->off_units = res.image[pka::kHdrOffUnits];
   p->off_req = res.image[pka::kHdrOffReq];
   p->off_merge = res.image[pka::kHdrOffMerge];
   p->off_idx = res.image[pka::kHdrOffIndices];
   p->off_sched = res.image[pka::kHdrOffSched];
+  if (pl.mp.mixed) {
+    const pka::MixedPlan& mp = pl.mp;
+    p->num_parts = 2;
+    p->parts[0] = {mp.prefill.kernel, mp.prefill.num_workers, mp.prefill.num_merge, mp.off_prefill, 0};
+    p->parts[1] = {mp.decode.kernel, mp.decode.num_workers, mp.decode.num_merge, mp.off_decode,
+                   mp.float_off_decode};
+  } else {
+    p->num_parts = 1;
+    p->parts[0] = {res.kernel, res.num_workers, res.num_merge, 0, 0};
+  }
   return PKA_OK;
 }
 
@@ -156,16 +215,16 @@ KvLayout standard_layout(const pka_plan* p) {
   return {2 * static_cast<int64_t>(p->page_size) * row, row, p->head_dim};
 }
 
-pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const void* v, const KvLayout& kv,
-                        void* o, float* lse) {
+pka::AttnArgs attn_args(const pka_plan* p, const PartLaunch& part, const void* q, const void* k, const void* v,
+                        const KvLayout& kv, void* o, float* lse) {
   pka::AttnArgs a{};
-  const int32_t* iw = static_cast<const int32_t*>(p->int_ws);
+  const int32_t* iw = static_cast<const int32_t*>(p->int_ws) + part.off_words;
   a.q = static_cast<const uint16_t*>(q);
   a.k = static_cast<const uint16_t*>(k);
   a.v = static_cast<const uint16_t*>(v);
   a.o = o;
   a.lse = lse;
-  a.part_o = static_cast<float*>(p->float_ws);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(p->float_ws) + part.float_off);
   a.ws = const_cast<int32_t*>(iw);
   const bool ragged = p->flags & PKA_RAGGED_KV;
   a.page_size = ragged ? 1 : p->page_size;
@@ -183,23 +242,19 @@ pka::AttnArgs attn_args(const pka_plan* p, const void* q, const void* k, const v
   return a;
 }
 
-int run_common(const pka_plan* p, const void* q, const void* k, const void* v, const KvLayout& kv, void* o,
-               float* lse, hipStream_t stream) {
-  // A graph-stable plan always enqueues the same launches (a captured run is
-  // replayed for later batches); the kernels find an empty batch empty.
+// One part's attention launch and, if it split any KV, its merge.
+int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const void* k, const void* v,
+             const KvLayout& kv, void* o, float* lse, hipStream_t stream) {
   const bool stable = (p->flags & PKA_GRAPH_STABLE) != 0;
-  if (p->info.total_q == 0 && !stable) return PKA_OK;
-  if (!q || !o) return set_error(PKA_ERR_INVALID_ARG, "q and o must not be NULL");
-  if (p->info.total_kv > 0 && !k) return set_error(PKA_ERR_INVALID_ARG, "KV pointer must not be NULL");
-  const pka::AttnArgs a = attn_args(p, q, k, v, kv, o, lse);
+  const pka::AttnArgs a = attn_args(p, part, q, k, v, kv, o, lse);
   const bool paged = !(p->flags & PKA_RAGGED_KV);
   hipError_t e;
-  if (p->info.kernel == PKA_KERNEL_DECODE)
-    e = pka::launch_decode(a, p->head_dim, paged, p->info.num_workers, stream);
+  if (part.kernel == PKA_KERNEL_DECODE)
+    e = pka::launch_decode(a, p->head_dim, paged, part.num_workers, stream);
   else
-    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, p->info.num_workers, stream);
+    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, part.num_workers, stream);
   if (e != hipSuccess) return hip_error("attention launch", e);
-  if (p->info.num_merge_groups > 0 || stable) {
+  if (part.num_merge > 0 || stable) {
     pka::MergeArgs m{};
     m.part_o = a.part_o;
     m.ws = a.ws;
@@ -208,9 +263,37 @@ int run_common(const pka_plan* p, const void* q, const void* k, const void* v, c
     m.num_qo_heads = p->num_qo_heads;
     m.group = p->group;
     m.out_fp32 = a.out_fp32;
-    e = pka::launch_merge(m, p->head_dim, stable ? pka::kMergeGrid : p->info.num_merge_groups, stream);
+    e = pka::launch_merge(m, p->head_dim, stable ? pka::kMergeGrid : part.num_merge, stream);
     if (e != hipSuccess) return hip_error("merge launch", e);
   }
+  return PKA_OK;
+}
+
+int run_common(const pka_plan* p, const void* q, const void* k, const void* v, const KvLayout& kv, void* o,
+               float* lse, hipStream_t stream) {
+  // A graph-stable plan always enqueues the same launches (a captured run is
+  // replayed for later batches); the kernels find an empty batch empty.
+  const bool stable = (p->flags & PKA_GRAPH_STABLE) != 0;
+  if (p->info.total_q == 0 && !stable) return PKA_OK;
+  if (!q || !o) return set_error(PKA_ERR_INVALID_ARG, "q and o must not be NULL");
+  if (p->info.total_kv > 0 && !k) return set_error(PKA_ERR_INVALID_ARG, "KV pointer must not be NULL");
+  if (p->num_parts == 1) return run_part(p, p->parts[0], q, k, v, kv, o, lse, stream);
+  // Mixed batch: the prefill launch goes first, on the caller's stream, so
+  // that its workgroups take their compute units before the decode launch
+  // (forked onto the plan's side stream) fills the rest; the caller's stream
+  // then waits for the side stream.  The two write disjoint output rows.
+  hipError_t e = hipEventRecord(p->fork, stream);
+  if (e != hipSuccess) return hip_error("hipEventRecord(fork)", e);
+  e = hipStreamWaitEvent(p->side, p->fork, 0);
+  if (e != hipSuccess) return hip_error("hipStreamWaitEvent(fork)", e);
+  int st = run_part(p, p->parts[0], q, k, v, kv, o, lse, stream);
+  if (st != PKA_OK) return st;
+  st = run_part(p, p->parts[1], q, k, v, kv, o, lse, p->side);
+  if (st != PKA_OK) return st;
+  e = hipEventRecord(p->join, p->side);
+  if (e != hipSuccess) return hip_error("hipEventRecord(join)", e);
+  e = hipStreamWaitEvent(stream, p->join, 0);
+  if (e != hipSuccess) return hip_error("hipStreamWaitEvent(join)", e);
   return PKA_OK;
 }
 
@@ -230,11 +313,11 @@ int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
     const int32_t nnz = kv_indptr[batch];
     pka::PlanInput in = make_input(qo_indptr, kv_indptr, nullptr, kv_last_page_len, batch, nnz, 0,
                                    num_qo_heads, num_kv_heads, head_dim, page_size, causal, flags, false);
-    pka::PlanResult res;
+    Planned res;
     const int st = plan_or_error(in, &res);
     if (st != PKA_OK) return st;
-    *int_ws_bytes = res.image.size() * sizeof(int32_t);
-    *float_ws_bytes = res.float_ws_bytes;
+    *int_ws_bytes = res.image().size() * sizeof(int32_t);
+    *float_ws_bytes = res.float_ws_bytes();
     return PKA_OK;
   } catch (const std::exception& ex) {
     return set_error(PKA_ERR_INVALID_ARG, ex.what());
@@ -250,14 +333,14 @@ int pka_plan_host_image(const int32_t* qo_indptr, const int32_t* kv_indptr, cons
     pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
                                    num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
                                    causal, flags, true);
-    pka::PlanResult res;
+    Planned res;
     const int st = plan_or_error(in, &res);
     if (st != PKA_OK) return st;
-    if (info) fill_info(res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, info);
-    const size_t need = res.image.size() * sizeof(int32_t);
+    if (info) fill_plan_info(res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, info);
+    const size_t need = res.image().size() * sizeof(int32_t);
     if (image) {
       if (image_bytes < need) return set_error(PKA_ERR_WORKSPACE, "image buffer too small");
-      std::memcpy(image, res.image.data(), need);
+      std::memcpy(image, res.image().data(), need);
     }
     return PKA_OK;
   } catch (const std::exception& ex) {
@@ -278,16 +361,16 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
                                    num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
                                    causal, flags, true);
-    pka::PlanResult res;
+    Planned res;
     int st = plan_or_error(in, &res);
     if (st != PKA_OK) return st;
-    const size_t need = res.image.size() * sizeof(int32_t);
+    const size_t need = res.image().size() * sizeof(int32_t);
     if (int_ws_bytes < need)
       return set_error(PKA_ERR_WORKSPACE, "int workspace has " + std::to_string(int_ws_bytes) + " bytes, needs " +
                                               std::to_string(need));
-    if (float_ws_bytes < res.float_ws_bytes)
+    if (float_ws_bytes < res.float_ws_bytes())
       return set_error(PKA_ERR_WORKSPACE, "float workspace has " + std::to_string(float_ws_bytes) +
-                                              " bytes, needs " + std::to_string(res.float_ws_bytes));
+                                              " bytes, needs " + std::to_string(res.float_ws_bytes()));
     pka_plan* p = new pka_plan{};
     p->magic = kPlanMagic;
     p->num_qo_heads = num_qo_heads;
@@ -305,22 +388,34 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     p->float_ws_bytes = float_ws_bytes;
     p->staging = nullptr;
     p->staging_bytes = 0;
+    p->side = nullptr;
+    p->fork = p->join = nullptr;
     hipError_t e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
     if (e != hipSuccess) {
       delete p;
       return hip_error("hipEventCreateWithFlags(plan upload)", e);
     }
+    if (flags & PKA_MIXED_BATCH) {
+      // default priority, like every stream here
+      e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&p->fork, hipEventDisableTiming);
+      if (e == hipSuccess) e = hipEventCreateWithFlags(&p->join, hipEventDisableTiming);
+      if (e != hipSuccess) {
+        pka_plan_destroy(p);
+        return hip_error("plan side stream", e);
+      }
+    }
     st = upload(p, res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, stream);
     if (st != PKA_OK) {
-      (void)hipEventDestroy(p->uploaded);
-      if (p->staging) (void)hipHostFree(p->staging);
-      delete p;
+      pka_plan_destroy(p);
       return st;
     }
     if (env_int("PKA_LOG"))
-      std::fprintf(stderr, "[pka] plan: %s units=%d merge_groups=%d partial_rows=%d kv_chunk=%d int_ws=%zu float_ws=%zu\n",
-                   res.kernel == pka::kDecode ? "decode" : "prefill", res.num_units, res.num_merge,
-                   res.num_partial_rows, res.kv_chunk, need, res.float_ws_bytes);
+      std::fprintf(stderr, "[pka] plan: kernel=%d units=%d merge_groups=%d partial_rows=%d kv_chunk=%d "
+                   "workers=%d prefill_cus=%d decode_cus=%d int_ws=%zu float_ws=%lld\n",
+                   p->info.kernel, p->info.num_units, p->info.num_merge_groups, p->info.num_partial_rows,
+                   p->info.kv_chunk, p->info.num_workers, p->info.prefill_cus, p->info.decode_cus, need,
+                   static_cast<long long>(p->info.float_ws_bytes));
     *out = p;
     return PKA_OK;
   } catch (const std::exception& ex) {
@@ -416,6 +511,7 @@ int pka_debug_gather(const pka_plan* plan, const void* paged_kv, void* k_dense, 
                      pka_stream_t stream) {
   if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
   if (plan->flags & PKA_RAGGED_KV) return set_error(PKA_ERR_INVALID_ARG, "debug_gather needs a paged plan");
+  if (plan->num_parts != 1) return set_error(PKA_ERR_UNSUPPORTED, "debug_gather does not take a mixed-batch plan");
   if (plan->info.total_kv == 0) return PKA_OK;
   if (!paged_kv || !k_dense || !v_dense) return set_error(PKA_ERR_INVALID_ARG, "null pointer");
   pka::GatherArgs a{};
@@ -503,18 +599,19 @@ int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_
     pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
                                    plan->num_pages, plan->num_qo_heads, plan->num_kv_heads, plan->head_dim,
                                    plan->page_size, plan->causal, plan->flags, true);
-    pka::PlanResult res;
+    Planned res;
     const int st = plan_or_error(in, &res);
     if (st != PKA_OK) return st;
-    const size_t need = res.image.size() * sizeof(int32_t);
+    const size_t need = res.image().size() * sizeof(int32_t);
     if (plan->int_ws_bytes < need)
       return set_error(PKA_ERR_WORKSPACE, "int workspace has " + std::to_string(plan->int_ws_bytes) +
                                               " bytes, needs " + std::to_string(need));
-    if (plan->float_ws_bytes < res.float_ws_bytes)
+    if (plan->float_ws_bytes < res.float_ws_bytes())
       return set_error(PKA_ERR_WORKSPACE, "float workspace has " + std::to_string(plan->float_ws_bytes) +
-                                              " bytes, needs " + std::to_string(res.float_ws_bytes));
+                                              " bytes, needs " + std::to_string(res.float_ws_bytes()));
+    const pka::PlanResult& one = res.mp.single;
     if ((plan->flags & PKA_GRAPH_STABLE) &&
-        (res.kernel != plan->info.kernel || res.num_workers != plan->info.num_workers))
+        (one.kernel != plan->info.kernel || one.num_workers != plan->info.num_workers))
       return set_error(PKA_ERR_INVALID_ARG,
                        "a graph-stable plan cannot switch between prefill and decode batches");
     return upload(plan, res, batch, (plan->flags & PKA_RAGGED_KV) ? 0 : nnz_pages, stream);
@@ -526,6 +623,9 @@ int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_
 void pka_plan_destroy(pka_plan* plan) {
   if (!plan_ok(plan)) return;
   (void)hipEventDestroy(plan->uploaded);
+  if (plan->fork) (void)hipEventDestroy(plan->fork);
+  if (plan->join) (void)hipEventDestroy(plan->join);
+  if (plan->side) (void)hipStreamDestroy(plan->side);
   if (plan->staging) (void)hipHostFree(plan->staging);
   plan->magic = 0;
   delete plan;

@@ -310,9 +310,9 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   int64_t dense = 0;
   for (int r = 0; r < B; ++r) {
     int32_t* q = im + off_req + int64_t(r) * kReqWords;
-    q[kReqQoBegin] = in.qo_indptr[r];
+    q[kReqQoBegin] = in.qo_begin ? in.qo_begin[r] : in.qo_indptr[r];
     q[kReqQoLen] = static_cast<int32_t>(qo_len[r]);
-    q[kReqKvBegin] = in.kv_indptr[r];
+    q[kReqKvBegin] = (ragged && in.kv_begin) ? in.kv_begin[r] : in.kv_indptr[r];
     q[kReqKvLen] = static_cast<int32_t>(kv_len[r]);
     q[kReqKvDense] = static_cast<int32_t>(dense);
     dense += kv_len[r];
@@ -339,6 +339,123 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   out->float_ws_bytes = out->partial_lse_offset +
                         (static_cast<size_t>(partial_rows) * sizeof(float) + 255) / 256 * 256;
   if (out->float_ws_bytes == 0) out->float_ws_bytes = 256;
+  return kOk;
+}
+
+int32_t mixed_prefill_cus(double prefill_flop, double decode_bytes, int32_t num_cus, int32_t num_xcds) {
+  const int32_t step = std::max(1, num_xcds);
+  int32_t best = step;
+  double best_t = -1.0;
+  for (int32_t p = step; p + step <= num_cus; p += step) {
+    const double tp = prefill_flop / (kPrefillFlopPerCuNs * p);
+    const double td = decode_bytes / std::min(kDecodeBytePerNs, kDecodeBytePerCuNs * (num_cus - p));
+    const double t = std::max(tp, td);
+    if (best_t < 0.0 || t <= best_t) {
+      best_t = t;
+      best = p;
+    }
+  }
+  return best;
+}
+
+int build_mixed_plan(const PlanInput& in, MixedPlan* out, std::string* err) {
+  *out = MixedPlan{};
+  // The whole batch is always planned first: it validates every array, with
+  // the batch's own request numbers in the messages.
+  PlanInput whole = in;
+  whole.flags &= ~kFlagMixed;
+  int st = build_plan(whole, &out->single, err);
+  if (st != kOk || !(in.flags & kFlagMixed)) return st;
+  if (in.flags & kFlagGraphStable)
+    return fail(err, kUnsupported, "a mixed-batch plan cannot be graph-stable");
+  const int B = in.batch;
+  const bool ragged = (in.flags & kFlagRagged) != 0;
+  const int G = in.num_qo_heads / in.num_kv_heads;
+  std::vector<int> pre, dec;
+  for (int r = 0; r < B; ++r) {
+    const int32_t n = in.qo_indptr[r + 1] - in.qo_indptr[r];
+    if (n > 1) pre.push_back(r);
+    else if (n == 1) dec.push_back(r);
+  }
+  if (pre.empty() || dec.empty() || G > kDecodeMaxGroup) return kOk;  // one kind: the whole-batch plan
+
+  // Sub-batch inputs: indptr arrays over the subset, offsets of the whole batch.
+  struct Sub {
+    std::vector<int32_t> qo_indptr{0}, kv_indptr{0}, kv_indices, last, qo_begin, kv_begin;
+  };
+  auto make = [&](const std::vector<int>& rs, Sub* sb, PlanInput* pi) {
+    for (int r : rs) {
+      sb->qo_indptr.push_back(sb->qo_indptr.back() + (in.qo_indptr[r + 1] - in.qo_indptr[r]));
+      sb->kv_indptr.push_back(sb->kv_indptr.back() + (in.kv_indptr[r + 1] - in.kv_indptr[r]));
+      if (!ragged && in.kv_indices)
+        sb->kv_indices.insert(sb->kv_indices.end(), in.kv_indices + in.kv_indptr[r],
+                              in.kv_indices + in.kv_indptr[r + 1]);
+      if (!ragged) sb->last.push_back(in.kv_last_page_len[r]);
+      sb->qo_begin.push_back(in.qo_indptr[r]);
+      sb->kv_begin.push_back(in.kv_indptr[r]);
+    }
+    *pi = whole;
+    pi->qo_indptr = sb->qo_indptr.data();
+    pi->kv_indptr = sb->kv_indptr.data();
+    pi->kv_indices = (!ragged && in.kv_indices) ? sb->kv_indices.data() : nullptr;
+    pi->kv_last_page_len = ragged ? nullptr : sb->last.data();
+    pi->batch = static_cast<int32_t>(rs.size());
+    pi->nnz_pages = ragged ? 0 : sb->kv_indptr.back();
+    pi->qo_begin = sb->qo_begin.data();
+    pi->kv_begin = sb->kv_begin.data();
+  };
+  Sub sp, sd;
+  PlanInput ip, id;
+  make(pre, &sp, &ip);
+  make(dec, &sd, &id);
+
+  // The compute-unit split, from the algorithmic work of each side.
+  auto kv_len_of = [&](int r) -> int64_t {
+    const int64_t span = in.kv_indptr[r + 1] - in.kv_indptr[r];
+    if (ragged) return span;
+    return span == 0 ? 0 : (span - 1) * in.page_size + in.kv_last_page_len[r];
+  };
+  double flop = 0.0, bytes = 0.0;
+  for (int r : pre) {
+    const int64_t n = in.qo_indptr[r + 1] - in.qo_indptr[r], kv = kv_len_of(r);
+    double pairs = 0.0;  // visible (query, key) pairs
+    for (int64_t i = 0; i < n; ++i) {
+      const int64_t lim = in.causal ? std::min<int64_t>(kv, i + kv - n + 1) : kv;
+      pairs += static_cast<double>(std::max<int64_t>(0, lim));
+    }
+    flop += 4.0 * in.head_dim * in.num_qo_heads * pairs;
+  }
+  for (int r : dec) bytes += 4.0 * in.num_kv_heads * in.head_dim * static_cast<double>(kv_len_of(r));
+  int32_t pcus = in.prefill_cus_override > 0 ? in.prefill_cus_override
+                                             : mixed_prefill_cus(flop, bytes, in.num_cus, in.num_xcds);
+  pcus = std::max(1, std::min(pcus, in.num_cus - 1));
+  ip.num_cus = pcus;
+  id.num_cus = in.num_cus - pcus;
+
+  st = build_plan(ip, &out->prefill, err);
+  if (st != kOk) return st;
+  st = build_plan(id, &out->decode, err);
+  if (st != kOk) return st;
+  out->mixed = true;
+  out->prefill_cus = pcus;
+  out->decode_cus = in.num_cus - pcus;
+  out->off_prefill = kMixWords;
+  out->off_decode = out->off_prefill + align_words(static_cast<int64_t>(out->prefill.image.size()));
+  out->float_off_decode = (out->prefill.float_ws_bytes + 255) / 256 * 256;
+  out->float_ws_bytes = out->float_off_decode + out->decode.float_ws_bytes;
+  out->image.assign(static_cast<size_t>(out->off_decode) + out->decode.image.size(), 0);
+  int32_t* im = out->image.data();
+  im[kMixMagic] = kMixedMagic;
+  im[kMixKernel] = kMixed;
+  im[kMixOffPrefill] = out->off_prefill;
+  im[kMixOffDecode] = out->off_decode;
+  im[kMixFloatOffDecode] = static_cast<int32_t>(out->float_off_decode / sizeof(float));
+  im[kMixPrefillCus] = out->prefill_cus;
+  im[kMixDecodeCus] = out->decode_cus;
+  im[kMixBatch] = B;
+  im[kMixNnz] = ragged ? 0 : in.kv_indptr[B];
+  std::memcpy(im + out->off_prefill, out->prefill.image.data(), out->prefill.image.size() * sizeof(int32_t));
+  std::memcpy(im + out->off_decode, out->decode.image.data(), out->decode.image.size() * sizeof(int32_t));
   return kOk;
 }
 

@@ -98,7 +98,7 @@ enum SchedField : int {
   kSchedWords = 64
 };
 
-enum Kernel : int { kPrefill = 0, kDecode = 1 };
+enum Kernel : int { kPrefill = 0, kDecode = 1, kMixed = 2 };
 
 // Tile shapes the kernels are built for.
 constexpr int kPrefillBlockKeys = 64;   // keys per prefill KV tile
@@ -112,6 +112,7 @@ constexpr uint32_t kFlagDisableSplit = 0x1u;
 constexpr uint32_t kFlagOutFp32 = 0x2u;
 constexpr uint32_t kFlagRagged = 0x4u;
 constexpr uint32_t kFlagGraphStable = 0x8u;  // launch shapes that do not depend on the batch
+constexpr uint32_t kFlagMixed = 0x10u;       // prefill and decode requests as two concurrent launches
 
 enum Status : int { kOk = 0, kInvalid = 1, kUnsupported = 2, kWorkspace = 3, kHip = 4 };
 
@@ -133,6 +134,12 @@ struct PlanInput {
   int32_t kv_chunk_override = 0;  // >0: keys per split chunk (tuning); 0: heuristic
   int32_t num_cus = 256;          // compute units the split heuristic aims to fill
   int32_t num_xcds = 8;           // XCDs workgroups are dealt to round-robin (prefill order)
+  // Optional per-request overrides of where a request's rows and (ragged) K/V
+  // rows start, used for the sub-batches of a mixed plan: they keep the
+  // offsets of the whole batch while the indptr arrays describe the subset.
+  const int32_t* qo_begin = nullptr;
+  const int32_t* kv_begin = nullptr;
+  int32_t prefill_cus_override = 0;  // >0: compute units of a mixed plan's prefill launch (tuning)
 };
 
 // Prefill workgroup shape per head_dim: 32 packed query rows per wave, 8
@@ -161,5 +168,54 @@ struct PlanResult {
 
 // Validate and plan.  Returns a Status and fills *err on failure.
 int build_plan(const PlanInput& in, PlanResult* out, std::string* err);
+
+// A mixed batch (kFlagMixed with both prefill requests, qo_len > 1, and
+// decode requests, qo_len == 1) runs as two persistent launches side by
+// side: the prefill kernel on part of the compute units and the decode
+// kernel on the rest, each planned over its own requests as an ordinary
+// image.  The int workspace holds a 64-word header, then the prefill image,
+// then the decode image; the float workspace holds the prefill partial
+// states, then the decode ones.
+enum MixedField : int {
+  kMixMagic = 0,
+  kMixKernel,          // kMixed
+  kMixOffPrefill,      // word offset of the prefill image
+  kMixOffDecode,       // word offset of the decode image
+  kMixFloatOffDecode,  // float offset of the decode partial states
+  kMixPrefillCus,
+  kMixDecodeCus,
+  kMixBatch,
+  kMixNnz,
+  kMixWords = 64
+};
+constexpr int32_t kMixedMagic = 0x4d414b50;  // "PKAM"
+
+// Rates the compute-unit split is sized with, measured on MI355X with the
+// kernels here: the prefill kernel retires about kPrefillFlopPerCuNs flop per
+// ns per compute unit; the decode kernel streams about kDecodeBytePerCuNs
+// bytes per ns per compute unit and kDecodeBytePerNs in all.
+constexpr double kPrefillFlopPerCuNs = 3500.0;
+constexpr double kDecodeBytePerCuNs = 30.0;
+constexpr double kDecodeBytePerNs = 5800.0;
+
+struct MixedPlan {
+  bool mixed = false;      // false: `single` is the whole plan
+  PlanResult single;       // the plan of the whole batch (always built: it validates)
+  PlanResult prefill, decode;
+  int32_t prefill_cus = 0, decode_cus = 0;
+  int32_t off_prefill = 0, off_decode = 0;  // words
+  size_t float_off_decode = 0;              // bytes
+  std::vector<int32_t> image;               // mixed: header + both images
+  size_t float_ws_bytes = 0;
+};
+
+// Compute units for the prefill launch of a mixed batch: the multiple of
+// num_xcds that minimises the later of the two launches' ends under the
+// rates above (ties: more prefill units).
+int32_t mixed_prefill_cus(double prefill_flop, double decode_bytes, int32_t num_cus, int32_t num_xcds);
+
+// Plan a batch, as two sub-batches when in.flags has kFlagMixed and the
+// batch mixes both kinds of request (else as build_plan does).
+int build_mixed_plan(const PlanInput& in, MixedPlan* out, std::string* err);
 
 }  // namespace pka

@@ -248,6 +248,29 @@ def batch_decode(seed=5, batch=256, kv_log2_range=(7.0, 15.0), kv_clamp=(128, 32
                  pool_slack=0.02, gen=gen, poison=kw.pop("poison", True), **kw)
 
 
+def mixed_batch(seed=9, num_prefill=4, num_decode=192, prefix_range=(1024, 8192),
+                chunk_range=(512, 2048), kv_log2_range=(7.0, 14.0), kv_clamp=(128, 16384),
+                **kw) -> Workload:
+    """One step of chunked-prefill serving: num_prefill prefill chunks (prefix
+    P ~ U{...} cached, chunk n ~ U{...} appended: qo_len = n, kv_len = P + n)
+    and num_decode single-token requests (kv_len = clamp(round(2^U(a, b)))),
+    in a seeded random order; Hq=32, Hkv=8, D=128, page_size=16, causal,
+    permuted pages with 5% slack."""
+    gen = torch.Generator("cpu").manual_seed(seed)
+    P = _uniform_int(gen, prefix_range[0], prefix_range[1], num_prefill)
+    n = _uniform_int(gen, chunk_range[0], chunk_range[1], num_prefill)
+    a, b = kv_log2_range
+    u = torch.rand(num_decode, generator=gen, dtype=torch.float64) * (b - a) + a
+    kv_d = [int(min(max(round(2.0 ** float(x)), kv_clamp[0]), kv_clamp[1])) for x in u]
+    order = torch.randperm(num_prefill + num_decode, generator=gen).tolist()
+    reqs = [(n[i], P[i] + n[i]) for i in range(num_prefill)] + [(1, k) for k in kv_d]
+    qo = [reqs[i][0] for i in order]
+    kv = [reqs[i][1] for i in order]
+    return build("mixed_batch", seed, qo, kv, kw.pop("heads", 32), kw.pop("kv_heads", 8),
+                 kw.pop("head_dim", 128), kw.pop("page_size", 16), causal=True, pool_slack=0.05,
+                 gen=gen, notes={"num_prefill": num_prefill, "num_decode": num_decode}, **kw)
+
+
 def p5_shape(seed=6, batch=4, max_len=700, **kw) -> Workload:
     """Hq=16, Hkv=1, D=128, page_size=64, causal prefill with qo = kv ~ U{1..700}
     (the shape named gqa_paged_prefill_causal_h16_kv1_d128_ps64)."""
@@ -264,6 +287,7 @@ WORKLOADS = {
     "long_causal": long_causal,
     "batch_decode": batch_decode,
     "p5_shape": p5_shape,
+    "mixed_batch": mixed_batch,
 }
 
 

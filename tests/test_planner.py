@@ -53,7 +53,8 @@ def _cdiv(a, b):
     return -(-a // b)
 
 
-def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, flags, ragged=False, D=128):
+def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, flags, ragged=False, D=128,
+                 num_cus=NUM_CUS, qo_begin=None, kv_begin=None):
     B = len(qo_indptr) - 1
     G = Hq // Hkv
     qo_len = [qo_indptr[r + 1] - qo_indptr[r] for r in range(B)]
@@ -86,11 +87,11 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     if not (flags & pka.PKA_DISABLE_SPLIT_KV) and blocks:
         if decode:
             keys = sum(b[4] for b in blocks)
-            chunk = _cdiv(keys, NUM_CUS * 8)
+            chunk = _cdiv(keys, num_cus * 8)
             chunk = min(2048, max(256, _cdiv(chunk, 128) * 128))
-        elif len(blocks) < 2 * NUM_CUS:
+        elif len(blocks) < 2 * num_cus:
             tiles = sum(_cdiv(b[4], BLOCK_KEYS) for b in blocks)
-            chunk = max(8, _cdiv(tiles, 4 * NUM_CUS)) * BLOCK_KEYS
+            chunk = max(8, _cdiv(tiles, 4 * num_cus)) * BLOCK_KEYS
     units, merge, partial, any_split = [], [], 0, False
     for (r, hk, r0, r1, hi) in blocks:
         n = _cdiv(hi, chunk) if (chunk and hi > chunk) else 1
@@ -139,7 +140,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             bounds.append(len(order))
     nq = len(bounds) - 1
     longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
-    slots = NUM_CUS * (2 if decode else wg_per_cu(D))
+    slots = num_cus * (2 if decode else wg_per_cu(D))
     per_queue = max(1, slots // nq) if fixed else max(1, min(longest, max(1, slots // nq)))
     workers = nq * per_queue
     align = lambda w: _cdiv(w, 64) * 64
@@ -162,12 +163,72 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
         img[off_units + 8 * i: off_units + 8 * i + 8] = u
     dense = 0
     for r in range(B):
-        img[off_req + 8 * r: off_req + 8 * r + 5] = [qo_indptr[r], qo_len[r], kv_indptr[r], kv_len[r], dense]
+        img[off_req + 8 * r: off_req + 8 * r + 5] = [
+            qo_indptr[r] if qo_begin is None else qo_begin[r], qo_len[r],
+            kv_begin[r] if (ragged and kv_begin is not None) else kv_indptr[r], kv_len[r], dense]
         dense += kv_len[r]
     for g, m in enumerate(merge):
         img[off_merge + 8 * g: off_merge + 8 * g + 8] = m
     if nnz:
         img[off_idx: off_idx + nnz] = list(kv_indices)
+    return img
+
+
+# Compute-unit split of a mixed batch (planner.h: rates in flop and bytes per
+# ns, per compute unit, and the decode total).
+PREFILL_FLOP_PER_CU_NS, DECODE_BYTE_PER_CU_NS, DECODE_BYTE_PER_NS = 3500.0, 30.0, 5800.0
+
+
+def restate_mixed_cus(flop, nbytes, num_cus=NUM_CUS, step=NUM_XCDS):
+    best, best_t = step, None
+    for p in range(step, num_cus - step + 1, step):
+        t = max(flop / (PREFILL_FLOP_PER_CU_NS * p),
+                nbytes / min(DECODE_BYTE_PER_NS, DECODE_BYTE_PER_CU_NS * (num_cus - p)))
+        if best_t is None or t <= best_t:
+            best, best_t = p, t
+    return best
+
+
+def restate_mixed(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, flags, ragged=False, D=128):
+    """The image of a PKA_MIXED_BATCH plan: a 64-word header, then the
+    prefill sub-batch's image, then the decode sub-batch's; each sub-batch is
+    planned as an ordinary batch over its own requests (in batch order) with
+    the whole batch's row offsets, on its share of the compute units."""
+    B = len(qo_indptr) - 1
+    qo_len = [qo_indptr[r + 1] - qo_indptr[r] for r in range(B)]
+    pre = [r for r in range(B) if qo_len[r] > 1]
+    dec = [r for r in range(B) if qo_len[r] == 1]
+    plain = flags & ~pka.PKA_MIXED_BATCH
+    if not pre or not dec or Hq // Hkv > DECODE_MAX_G:
+        return restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, plain, ragged, D)
+
+    def kv_len(r):
+        span = kv_indptr[r + 1] - kv_indptr[r]
+        return span if ragged else (0 if span == 0 else (span - 1) * ps + last[r])
+
+    flop = sum(4.0 * D * Hq * pka.visible_pairs([qo_len[r]], [kv_len(r)], causal) for r in pre)
+    nbytes = sum(4.0 * Hkv * D * kv_len(r) for r in dec)
+    pcus = restate_mixed_cus(flop, nbytes)
+
+    def sub(rs, cus):
+        qi, ki, idx = [0], [0], []
+        for r in rs:
+            qi.append(qi[-1] + qo_len[r])
+            ki.append(ki[-1] + kv_indptr[r + 1] - kv_indptr[r])
+            if not ragged:
+                idx += kv_indices[kv_indptr[r]:kv_indptr[r + 1]]
+        return restate_plan(qi, ki, idx, None if ragged else [last[r] for r in rs], Hq, Hkv, ps, causal, plain,
+                            ragged, D, num_cus=cus, qo_begin=[qo_indptr[r] for r in rs],
+                            kv_begin=[kv_indptr[r] for r in rs])
+
+    ip, idc = sub(pre, pcus), sub(dec, NUM_CUS - pcus)
+    align = lambda w: _cdiv(w, 64) * 64
+    off_d = 64 + align(len(ip))
+    partial, part_lse = ip[10], ip[17]
+    float_ws_p = max(256, part_lse * 4 + _cdiv(partial * 4, 256) * 256)  # at least 256 bytes
+    hdr = [0x4d414b50, 2, 64, off_d, _cdiv(float_ws_p, 256) * 256 // 4, pcus, NUM_CUS - pcus, B,
+           0 if ragged else kv_indptr[B]]
+    img = hdr + [0] * (64 - len(hdr)) + ip + [0] * (off_d - 64 - len(ip)) + idc
     return img
 
 
@@ -421,3 +482,107 @@ def test_empty_batch_and_edge_lengths():
     # kv_len 0 and qo_len 0 requests plan without error
     w = W.build("edge", 3, [3, 0, 70, 1], [0, 5, 20, 1], 4, 2, 64, 4, causal=True, pool_slack=0.5)
     _image(w)
+
+
+# ---------------------------------------------------------------------------
+# Mixed prefill + decode batches (PKA_MIXED_BATCH)
+# ---------------------------------------------------------------------------
+
+def _mixed_random(seed):
+    rng = random.Random(1000 + seed)
+    B = rng.randint(2, 12)
+    Hkv = rng.choice([1, 2, 8])
+    G = rng.choice([1, 4, 8])
+    ps = rng.choice([1, 4, 16])
+    qo = [rng.choice([0, 1, 1, 1, rng.randint(2, 300)]) for _ in range(B)]
+    i, j = rng.sample(range(B), 2)  # at least one request of each kind
+    qo[i], qo[j] = rng.randint(2, 300), 1
+    kv = [rng.choice([0, rng.randint(1, 50), rng.randint(50, 3000)]) for _ in range(B)]
+    kv = [max(k, q) for k, q in zip(kv, qo)]
+    return W.build("mixed", seed, qo, kv, Hkv * G, Hkv, rng.choice([64, 128]), ps, causal=rng.random() < 0.8,
+                   pool_slack=0.2, poison=False)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_mixed_restatement(seed):
+    w = _mixed_random(seed)
+    flags = pka.PKA_MIXED_BATCH
+    img, info = _image(w, flags)
+    want = restate_mixed(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
+                         w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size, w.causal,
+                         flags, D=w.head_dim)
+    assert img.tolist() == want
+    assert info["kernel"] == pka.PKA_KERNEL_MIXED
+    assert info["prefill_cus"] + info["decode_cus"] == NUM_CUS and info["prefill_cus"] % NUM_XCDS == 0
+    a, b = pka.workspace_size(w.qo_indptr, w.kv_indptr, w.kv_last_page_len, w.num_qo_heads, w.num_kv_heads,
+                              w.head_dim, w.page_size, w.causal, flags)
+    assert a == info["int_ws_bytes"] == img.numel() * 4 and b == info["float_ws_bytes"]
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_mixed_coverage(seed):
+    """Both sub-plans together cover every visible (request, head, row, key)
+    once: prefill requests only in the prefill image, decode requests only in
+    the decode image (each sub-request is mapped back through its row offset)."""
+    w = _mixed_random(seed)
+    img, _ = _image(w, pka.PKA_MIXED_BATCH)
+    h = img[:64].tolist()
+    by_row = {int(w.qo_indptr[r]): r for r in range(w.batch) if w.qo_lens[r] > 0}
+    G = w.num_qo_heads // w.num_kv_heads
+    covered = {}
+    for off, end, kind in ((h[2], h[3], pka.PKA_KERNEL_PREFILL), (h[3], img.numel(), pka.PKA_KERNEL_DECODE)):
+        sub = img[off:end]
+        sh, units, req, _, _ = _unpack(sub)
+        assert sh[0] == 0x31414b50 and sh[1] == kind
+        for u in units:
+            sr, hk, r0, r1, lo, hi = u[:6]
+            r = by_row[req[sr][0]]
+            assert (w.qo_lens[r] == 1) == (kind == pka.PKA_KERNEL_DECODE)
+            assert req[sr][1] == w.qo_lens[r] and req[sr][3] == w.kv_lens[r]
+            for p in range(r0, r1):
+                covered.setdefault((r, hk, p), []).append((lo, hi))
+    for r in range(w.batch):
+        qo, kv = w.qo_lens[r], w.kv_lens[r]
+        for hk in range(w.num_kv_heads):
+            for p in range(qo * G):
+                i = p // G
+                vis_hi = kv if not w.causal else max(0, min(kv, i + kv - qo + 1))
+                pos = 0
+                for lo, hi in sorted(covered.get((r, hk, p), [])):
+                    assert lo == pos
+                    pos = hi
+                assert pos >= vis_hi
+
+
+def test_mixed_one_kind_plans_as_without_flag():
+    for w in (W.gqa_append(batch=3, prefix_range=(10, 90), chunk_range=(2, 20)), W.batch_decode(batch=7)):
+        a, ia = _image(w, pka.PKA_MIXED_BATCH)
+        b, ib = _image(w, 0)
+        # identical but for the flags word of the header
+        a[13] = b[13]
+        assert torch.equal(a, b) and ia["kernel"] == ib["kernel"]
+
+
+def test_mixed_named_workload_split():
+    """The chunked-prefill serving step: both kinds present, the split follows
+    the restated cost model."""
+    w = W.mixed_batch(num_decode=24, num_prefill=2, prefix_range=(100, 400), chunk_range=(50, 120))
+    img, info = _image(w, pka.PKA_MIXED_BATCH)
+    want = restate_mixed(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
+                         w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size, w.causal,
+                         pka.PKA_MIXED_BATCH, D=w.head_dim)
+    assert img.tolist() == want and info["kernel"] == pka.PKA_KERNEL_MIXED
+
+
+def test_mixed_cu_split_extremes():
+    assert restate_mixed_cus(1e12, 0.0) == NUM_CUS - NUM_XCDS        # decode has nothing to do
+    # prefill has nothing to do: decode gets the units it can use (its total
+    # rate saturates at 5800 / 30 = 193.3 units), ties go to prefill
+    assert restate_mixed_cus(0.0, 1e9) == 56
+    p = restate_mixed_cus(4.0e11, 2.6e9)
+    assert NUM_XCDS < p < NUM_CUS - NUM_XCDS
+
+
+def test_mixed_rejects_graph_stable():
+    w = W.mixed_batch(num_decode=4, num_prefill=1, prefix_range=(10, 40), chunk_range=(5, 9))
+    _expect(pka.PKA_ERR_UNSUPPORTED, lambda: _image(w, pka.PKA_MIXED_BATCH | pka.PKA_GRAPH_STABLE))
