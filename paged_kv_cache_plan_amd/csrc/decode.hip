@@ -77,15 +77,14 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
   // fields of a unit and of its request (wave-uniform)
   struct Unit { int hk, kv_lo, kv_hi, prow, qo_begin, kv_base; };
   auto load_unit = [&](int ui) {
-    const int32_t* u = pv.units + static_cast<int64_t>(ui) * 8;
+    const int32_t* u = pv.units + static_cast<int64_t>(ui) * kUnitWords;
     Unit x;
-    x.hk = u[1];
-    x.kv_lo = u[4];
-    x.kv_hi = u[5];
-    x.prow = u[6];
-    const int32_t* rq = pv.req + static_cast<int64_t>(u[0]) * 8;
-    x.qo_begin = rq[0];
-    x.kv_base = rq[2];
+    x.hk = u[kUnitKvHead];
+    x.kv_lo = u[kUnitKvBegin];
+    x.kv_hi = u[kUnitKvEnd];
+    x.prow = u[kUnitPartialRow];
+    x.qo_begin = u[kUnitQoBegin];
+    x.kv_base = u[kUnitKvBase];
     return x;
   };
 

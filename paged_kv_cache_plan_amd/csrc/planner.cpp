@@ -186,6 +186,10 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
       u.f[kUnitKvEnd] = static_cast<int32_t>(hi);
       u.f[kUnitPartialRow] = n_split > 1 ? static_cast<int32_t>(pbase + s * nrows) : -1;
       u.f[kUnitReserved] = 0;
+      u.f[kUnitQoBegin] = in.qo_begin ? in.qo_begin[b.r] : in.qo_indptr[b.r];
+      u.f[kUnitQoLen] = static_cast<int32_t>(qo_len[b.r]);
+      u.f[kUnitKvBase] = (ragged && in.kv_begin) ? in.kv_begin[b.r] : in.kv_indptr[b.r];
+      u.f[kUnitKvLen] = static_cast<int32_t>(kv_len[b.r]);
       u.cost = (hi - lo) * nrows + 1;
       u.seq = static_cast<int32_t>(units.size());
       units.push_back(u);

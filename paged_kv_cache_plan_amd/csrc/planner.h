@@ -43,7 +43,9 @@ enum HeaderField : int {
 };
 constexpr int32_t kMagic = 0x31414b50;  // "PKA1"
 
-// One work unit = one workgroup of the attention launch.
+// One work unit = one workgroup of the attention launch.  Words 8-11 copy
+// the request's fields, so that a kernel starting a unit waits for one
+// record load instead of two dependent ones.
 enum UnitField : int {
   kUnitRequest = 0,
   kUnitKvHead,
@@ -53,7 +55,11 @@ enum UnitField : int {
   kUnitKvEnd,     // one past the last key
   kUnitPartialRow,  // -1: write o/lse; otherwise first fp32 partial row
   kUnitReserved,
-  kUnitWords = 8
+  kUnitQoBegin,   // = the request's kReqQoBegin
+  kUnitQoLen,     // = kReqQoLen
+  kUnitKvBase,    // = kReqKvBegin
+  kUnitKvLen,     // = kReqKvLen
+  kUnitWords = 16
 };
 
 // Per-request facts the kernels need.

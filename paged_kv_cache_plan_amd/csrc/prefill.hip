@@ -72,20 +72,19 @@ struct UnitInfo {
 };
 
 __device__ __forceinline__ UnitInfo load_unit(const PlanView& pv, int ui) {
-  const int32_t* u = pv.units + static_cast<int64_t>(ui) * 8;
+  const int32_t* u = pv.units + static_cast<int64_t>(ui) * kUnitWords;
   UnitInfo x;
-  x.r = u[0];
-  x.hk = u[1];
-  x.row_begin = u[2];
-  x.row_end = u[3];
-  x.kv_lo = u[4];
-  x.kv_hi = u[5];
-  x.prow = u[6];
-  const int32_t* rq = pv.req + static_cast<int64_t>(x.r) * 8;
-  x.qo_begin = rq[0];
-  x.qo_len = rq[1];
-  x.kv_base = rq[2];
-  x.kv_len = rq[3];
+  x.r = u[kUnitRequest];
+  x.hk = u[kUnitKvHead];
+  x.row_begin = u[kUnitRowBegin];
+  x.row_end = u[kUnitRowEnd];
+  x.kv_lo = u[kUnitKvBegin];
+  x.kv_hi = u[kUnitKvEnd];
+  x.prow = u[kUnitPartialRow];
+  x.qo_begin = u[kUnitQoBegin];
+  x.qo_len = u[kUnitQoLen];
+  x.kv_base = u[kUnitKvBase];
+  x.kv_len = u[kUnitKvLen];
   return x;
 }
 

@@ -33,7 +33,7 @@ def block_rows(D):
 def wg_per_cu(D):
     return 1 if D == 128 else 2
 NUM_CUS, NUM_XCDS, QUEUE_WINDOW = 256, 8, 2
-UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 8, 8, 8
+UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 16, 8, 8
 
 
 def test_library_exports_every_declared_symbol():
@@ -105,7 +105,10 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
         for s_ in range(n):
             lo = s_ * chunk if n > 1 else 0
             up = min(hi, lo + chunk) if n > 1 else hi
-            units.append(([r, hk, r0, r1, lo, up, base + s_ * nrows if n > 1 else -1, 0],
+            # words 8-11 repeat the request's row offset, qo_len, KV base and kv_len
+            req_words = [qo_indptr[r] if qo_begin is None else qo_begin[r], qo_len[r],
+                         kv_begin[r] if (ragged and kv_begin is not None) else kv_indptr[r], kv_len[r]]
+            units.append(([r, hk, r0, r1, lo, up, base + s_ * nrows if n > 1 else -1, 0] + req_words + [0] * 4,
                           (up - lo) * nrows + 1, len(units)))
     key = lambda u: (-u[1], u[2])
     fixed = bool(flags & pka.PKA_GRAPH_STABLE)
@@ -160,7 +163,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     for q in range(nq):  # counters (words 0, 1) start at zero
         img[off_sched + 64 * q + 32: off_sched + 64 * q + 35] = [bounds[q], bounds[q + 1], per_queue]
     for i, u in enumerate(order):
-        img[off_units + 8 * i: off_units + 8 * i + 8] = u
+        img[off_units + UNIT_WORDS * i: off_units + UNIT_WORDS * (i + 1)] = u
     dense = 0
     for r in range(B):
         img[off_req + 8 * r: off_req + 8 * r + 5] = [
@@ -241,7 +244,7 @@ def _image(w, flags=0, causal=None):
 def _unpack(img):
     h = img[:16].tolist()
     n_units, n_merge, B = h[2], h[3], h[4]
-    units = img[h[6]: h[6] + 8 * n_units].view(-1, 8).tolist() if n_units else []
+    units = img[h[6]: h[6] + UNIT_WORDS * n_units].view(-1, UNIT_WORDS).tolist() if n_units else []
     req = img[h[7]: h[7] + 8 * B].view(-1, 8).tolist() if B else []
     merge = img[h[8]: h[8] + 8 * n_merge].view(-1, 8).tolist() if n_merge else []
     idx = img[h[9]: h[9] + h[5]].tolist()
@@ -285,7 +288,8 @@ def test_coverage_and_restatement(kind, seed, flags):
     G = w.num_qo_heads // w.num_kv_heads
     covered = {}
     for u in units:
-        r, hk, r0, r1, lo, hi, prow, _ = u
+        r, hk, r0, r1, lo, hi, prow = u[:7]
+        assert u[8:12] == req[r][:4]  # the request words repeated in the unit
         assert r0 < r1
         assert 0 <= lo <= hi <= w.kv_lens[r]
         for p in range(r0, r1):
