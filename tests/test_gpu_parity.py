@@ -115,6 +115,36 @@ def test_decode_head_dim_64_and_mha():
     compare(o, lse, *oracle_paged(w), "decode D=64 MHA")
 
 
+@pytest.mark.parametrize("ps,D,Hq,Hkv", [(1, 128, 32, 8), (3, 128, 32, 8), (7, 64, 4, 1), (16, 128, 16, 1),
+                                         (64, 128, 8, 2), (128, 64, 8, 8), (2, 64, 16, 16)])
+def test_decode_page_sizes_and_groups(ps, D, Hq, Hkv):
+    """Decode across the page-id modes (one id per row for page_size < 16
+    or not a power of two, two per 32-key step otherwise), group sizes up
+    to 16, with and without split KV; KV lengths include 1 and non-multiples
+    of the page size."""
+    w = W.batch_decode(seed=60 + ps + D, batch=12, kv_log2_range=(0.0, 11.5), kv_clamp=(1, 3000), head_dim=D,
+                       heads=Hq, kv_heads=Hkv, page_size=ps)
+    for split in (True, False):
+        o, lse, info = run_paged(w, disable_split_kv=not split)
+        assert info["kernel"] == pka.PKA_KERNEL_DECODE
+        compare(o, lse, *oracle_paged(w), f"decode ps={ps} D={D} G={Hq // Hkv} split={split}")
+
+
+def test_decode_ragged():
+    w = W.build("dec_ragged", 61, [1] * 9, [1, 5, 33, 64, 65, 700, 1500, 2, 2049], 16, 4, 128, 1, causal=True,
+                ragged=True, poison=False)
+    o, lse, info = run_ragged(w)
+    assert info["kernel"] == pka.PKA_KERNEL_DECODE
+    compare(o, lse, *oracle_paged(w), "decode ragged")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_prefill_non_causal(D):
+    w = W.build("nc", 62 + D, [130, 7, 300], [400, 7, 90], 8, 2, D, 16, causal=False, pool_slack=0.2)
+    o, lse, _ = run_paged(w)
+    compare(o, lse, *oracle_paged(w), f"non-causal D={D}")
+
+
 def test_prefill_split_kv():
     # few row blocks -> the planner splits the KV and merges afterwards
     w = W.build("split", 7, [40], [3000], 8, 2, 128, 16, causal=True, pool_slack=0.1)

@@ -88,7 +88,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
         if decode:
             keys = sum(b[4] for b in blocks)
             chunk = _cdiv(keys, num_cus * 8)
-            chunk = min(2048, max(256, _cdiv(chunk, 128) * 128))
+            chunk = min(16384, max(256, _cdiv(chunk, 128) * 128))
         elif len(blocks) < 2 * num_cus:
             tiles = sum(_cdiv(b[4], BLOCK_KEYS) for b in blocks)
             chunk = max(8, _cdiv(tiles, 4 * num_cus)) * BLOCK_KEYS
