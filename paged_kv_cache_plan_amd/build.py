@@ -6,7 +6,7 @@
 * the C ABI (host code against the HIP runtime) with hipcc;
 * the kernels with ``hipcc --offload-arch=gfx950 -O3`` and packed-fp32
   instruction selection switched off (``-Xclang -target-feature -Xclang
-  -packed-fp32-ops``);
+  -packed-fp32-ops``); decode also without the atomic optimizer;
 * everything is linked into ``paged_kv_cache_plan_amd/libpka.so``.
 
 A host-only ``libpka_planner_host.so`` (planner + a tiny C shim, no HIP) is
@@ -28,6 +28,10 @@ KERNELS = ["prefill.hip", "decode.hip", "merge.hip", "append.hip"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
+# decode takes its next unit with one lane's atomic whose result is awaited
+# only at the unit's end; the atomic optimizer would read it back at once
+# (a wait for every load in flight)
+KERNEL_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _hipcc() -> str:
@@ -78,7 +82,7 @@ def build(verbose: bool = False) -> str:
     for k in KERNELS:
         o = os.path.join(BUILD_DIR, k.replace(".hip", ".o"))
         kobjs.append(o)
-        cmds.append([hipcc, *HIP_FLAGS, *inc, "-c", os.path.join(CSRC, k), "-o", o])
+        cmds.append([hipcc, *HIP_FLAGS, *KERNEL_FLAGS.get(k, []), *inc, "-c", os.path.join(CSRC, k), "-o", o])
     _run_all(cmds, verbose)
     tmp = LIB_PATH + ".tmp"
     _run_all([[hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,

@@ -42,11 +42,12 @@ __device__ __forceinline__ int dvt_swz(int d) { return ((d >> 1) ^ (d >> 3)) & 3
 // page_size is a power of two >= 16 (each 16-key half of a step lies in one
 // page, so the whole wave shares two page ids), or any other page table (one
 // page id per row).
-enum IdMode : int { kRagged = 0, kPagedUniform = 1, kPagedLane = 2 };
+enum IdMode : int { kRagged = 0, kPagedUniform = 1, kPagedLane = 2, kPagedLaneDiv = 3 };
 
 template <int D, int MODE>
 __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnArgs a) {
   constexpr bool PAGED = MODE != kRagged;
+  constexpr bool LANE = MODE == kPagedLane || MODE == kPagedLaneDiv;  // page ids per lane
   constexpr int CPR = D / 8;   // 16-byte chunks per row
   constexpr int DS = D / 32;   // k-steps of the S^T MFMA
   constexpr int DB = D / 16;   // 16-row d blocks of O^T
@@ -78,13 +79,16 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
   struct Unit { int hk, kv_lo, kv_hi, prow, qo_begin, kv_base; };
   auto load_unit = [&](int ui) {
     const int32_t* u = pv.units + static_cast<int64_t>(ui) * kUnitWords;
+    // read as wave-uniform values, so that no later wait is left pending on
+    // these loads (a join with a path that never used them would keep one)
+    auto rd = [&](int w) { return __builtin_amdgcn_readfirstlane(u[w]); };
     Unit x;
-    x.hk = u[kUnitKvHead];
-    x.kv_lo = u[kUnitKvBegin];
-    x.kv_hi = u[kUnitKvEnd];
-    x.prow = u[kUnitPartialRow];
-    x.qo_begin = u[kUnitQoBegin];
-    x.kv_base = u[kUnitKvBase];
+    x.hk = rd(kUnitKvHead);
+    x.kv_lo = rd(kUnitKvBegin);
+    x.kv_hi = rd(kUnitKvEnd);
+    x.prow = rd(kUnitPartialRow);
+    x.qo_begin = rd(kUnitQoBegin);
+    x.kv_base = rd(kUnitKvBase);
     return x;
   };
 
@@ -115,29 +119,42 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
   struct IdsLane { int k[2]; int v[8]; };
   struct IdsNone {};
   using Ids = typename std::conditional<MODE == kPagedUniform, IdsUniform,
-                typename std::conditional<MODE == kPagedLane, IdsLane, IdsNone>::type>::type;
+                typename std::conditional<LANE, IdsLane, IdsNone>::type>::type;
+  // page of a key; the page size is a compile-time choice between a power of
+  // two and not, so no id load sits behind a branch
+  auto page_of = [&](int key) -> int {  // (keys are never negative)
+    return MODE == kPagedLaneDiv ? static_cast<unsigned>(key) / static_cast<unsigned>(ps) : key >> pshift;
+  };
+  // Keys past the unit's range read the row of its last key instead: a
+  // valid row whose score the mask sets to -inf, so its P is exactly zero.
+  // No load is then predicated, and no load result is copied or read as a
+  // wave-uniform value before its use, which would wait for every load in
+  // flight (the next step's prefetch included).
   auto fetch_ids = [&](int k0, Ids& id) {
+    const int last = kv_hi - 1;
     if constexpr (MODE == kPagedUniform) {
-      id.s[0] = pv.kv_indices[kv_base + (k0 >> pshift)];
-      id.s[1] = (k0 + 16 < kv_hi) ? pv.kv_indices[kv_base + ((k0 + 16) >> pshift)] : id.s[0];
-    } else if constexpr (MODE == kPagedLane) {
-      {
+      // per-lane copies of the two ids (VGPRs, not SGPRs)
+      int z = 0;
+      asm volatile("" : "+v"(z));
+      id.s[0] = pv.kv_indices[kv_base + (min(k0, last) >> pshift) + z];
+      id.s[1] = pv.kv_indices[kv_base + (min(k0 + 16, last) >> pshift) + z];
+    } else if constexpr (LANE) {
 #pragma unroll
-        for (int kb = 0; kb < 2; ++kb) {
-          const int key = k0 + 16 * kb + col;
-          id.k[kb] = key < kv_hi ? pv.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
-        }
+      for (int kb = 0; kb < 2; ++kb) {
+        const int key = min(k0 + 16 * kb + col, last);
+        id.k[kb] = pv.kv_indices[kv_base + page_of(key)];
+      }
 #pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const int key = k0 + v_key(j);
-          id.v[j] = (v_lane && key < kv_hi) ? pv.kv_indices[kv_base + (pshift >= 0 ? key >> pshift : key / ps)] : 0;
-        }
+      for (int j = 0; j < 8; ++j) {
+        const int key = min(k0 + v_key(j), last);
+        id.v[j] = pv.kv_indices[kv_base + page_of(key)];
       }
     }
   };
   auto row_off = [&](int key, int pid) -> int64_t {  // element offset of the K row of `key`
     if constexpr (PAGED) {
-      const int slot = pshift >= 0 ? (key & (ps - 1)) : (key % ps);
+      const int slot = MODE == kPagedLaneDiv ? static_cast<int>(static_cast<unsigned>(key) % static_cast<unsigned>(ps))
+                                            : (key & (ps - 1));
       return static_cast<int64_t>(pid) * a.page_stride + static_cast<int64_t>(slot) * a.row_stride;
     } else {
       return static_cast<int64_t>(kv_base + key) * a.page_stride;
@@ -145,45 +162,43 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
   };
   struct Data { u32x4 k[2][DS]; u32x4 v[8]; };
   auto fetch_data = [&](int k0, const Ids& id, Data& x) {
+    const int last = kv_hi - 1;
 #pragma unroll
     for (int kb = 0; kb < 2; ++kb) {
-      const int key = k0 + 16 * kb + col;
+      const int key = min(k0 + 16 * kb + col, last);
       int pid = 0;
       if constexpr (MODE == kPagedUniform) pid = id.s[kb];
-      if constexpr (MODE == kPagedLane) pid = id.k[kb];
-      if (key < kv_hi) {
-        const uint16_t* p = kb_ptr + row_off(key, pid) + 8 * g4;
+      if constexpr (LANE) pid = id.k[kb];
+      const uint16_t* p = kb_ptr + row_off(key, pid) + 8 * g4;
 #pragma unroll
-        for (int s = 0; s < DS; ++s) x.k[kb][s] = ld16(p + 32 * s);
-      } else {
-#pragma unroll
-        for (int s = 0; s < DS; ++s) x.k[kb][s] = u32x4{0, 0, 0, 0};
-      }
+      for (int s = 0; s < DS; ++s) x.k[kb][s] = ld16_stream(p + 32 * s);
     }
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      const int key = k0 + v_key(j);
+      const int key = min(k0 + v_key(j), last);
       int pid = 0;
       if constexpr (MODE == kPagedUniform) pid = id.s[j >> 2];
-      if constexpr (MODE == kPagedLane) pid = id.v[j];
-      x.v[j] = (v_lane && key < kv_hi) ? ld16(vb_ptr + row_off(key, pid) + 8 * vc) : u32x4{0, 0, 0, 0};
+      if constexpr (LANE) pid = id.v[j];
+      x.v[j] = ld16_stream(vb_ptr + row_off(key, pid) + 8 * vc);  // lanes past the 4 V groups load and ignore
     }
   };
 
-  // Steps t = wave, wave + 4, ...: page ids two steps ahead, data one ahead.
-  Ids ids_next{};
-  Data cur{}, nxt{};
+  // Steps t = wave, wave + 4, ...: page ids two steps ahead, data one ahead,
+  // each in two buffers that alternate from step to step (the first step of
+  // a unit reads buf_a, and ids_b holds the ids of its second step).
+  Ids ids_a{}, ids_b{};
+  Data buf_a{}, buf_b{};
   auto start_unit = [&](const Unit& U) {
     bind(U);
     const uint16_t* qp = a.q + (static_cast<int64_t>(U.qo_begin) * Hq + U.hk * G + (col_ok ? col : 0)) * D + 8 * g4;
 #pragma unroll
     for (int s = 0; s < DS; ++s) qreg[s] = as_bf16x8(col_ok ? ld16(qp + 32 * s) : u32x4{0, 0, 0, 0});
-    const int n = U.kv_hi > U.kv_lo ? (U.kv_hi - U.kv_lo + kTK - 1) / kTK : 0;
-    if (wave < n) {
-      Ids ids0{};
-      fetch_ids(U.kv_lo + wave * kTK, ids0);
-      fetch_data(U.kv_lo + wave * kTK, ids0, cur);
-      if (wave + kWaves < n) fetch_ids(U.kv_lo + (wave + kWaves) * kTK, ids_next);
+    if (U.kv_hi > U.kv_lo) {
+      // ids of the first two steps before the first data, so that waiting
+      // for the second step's ids does not wait for the first step's data
+      fetch_ids(U.kv_lo + wave * kTK, ids_a);
+      fetch_ids(U.kv_lo + (wave + kWaves) * kTK, ids_b);
+      fetch_data(U.kv_lo + wave * kTK, ids_a, buf_a);
     }
   };
 
@@ -205,18 +220,22 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
   const float sl2 = a.scale_log2;
 
   const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kTK - 1) / kTK : 0;
-  // wave 0 claims the next unit at its last step (at once if it has none);
-  // the first merge barrier publishes the claim
-  if (wave == 0 && wave >= n_tiles) claim(slot ^ 1);
-  int t = wave;
-  for (; t < n_tiles; t += kWaves) {
+  // Thread 0 takes the next unit as its wave starts its last step (at once
+  // if it has none) and writes the id to LDS after the steps (the first
+  // merge barrier publishes it), so the atomic's return is awaited only there.
+  int next_claim = 0;
+  // Every step issues the same loads (past the unit's end they are clamped,
+  // unused reads), so the compiler's load accounting stays exact and a step
+  // waits only for its own data, not for the prefetch behind it.
+  // The ids two steps ahead are issued before the next step's data, so the
+  // wait for the ids that data needs leaves that step's own data in flight.
+  auto step = [&](int t, Data& cur, Data& nxt, const Ids& ids_use, Ids& ids_fill) {
     const int k0 = kv_lo + t * kTK;
-    if (t + kWaves < n_tiles) {
-      fetch_data(k0 + kWaves * kTK, ids_next, nxt);
-      if (t + 2 * kWaves < n_tiles) fetch_ids(k0 + 2 * kWaves * kTK, ids_next);
-    } else if (wave == 0) {
-      claim(slot ^ 1);
-    }
+    fetch_ids(k0 + 2 * kWaves * kTK, ids_fill);
+    fetch_data(k0 + kWaves * kTK, ids_use, nxt);
+    // keep this step's work on `cur` below the loads (hoisted above them, it
+    // would wait for `cur` before they issue)
+    __builtin_amdgcn_sched_barrier(0);
 
     f32x4 s[2];
 #pragma unroll
@@ -229,6 +248,11 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
 
     // transpose V into the wave's V^T tile
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    // (an empty use by every lane, so that no path past the branch below
+    // sees these loads as still pending: a later write to their registers
+    // would wait for the newest loads)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) __asm__ volatile("" ::"v"(cur.v[j]));
     if (v_lane) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
@@ -290,10 +314,30 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
       const bf16x8 va = as_bf16x8(ld16(vt + d * kTK + ((g4 ^ dvt_swz(d)) * 8)));
       o[b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, pb, o[b], 0, 0, 0);
     }
-    cur = nxt;
+  };
+  // pairs of steps, then an odd last one: no path runs a step twice in a
+  // row on one buffer, which would leave its prefetch looking unfinished
+  const int my_steps = wave < n_tiles ? (n_tiles - 1 - wave) / kWaves + 1 : 0;
+  auto claim_at = [&](int i) {
+    if (tid == 0 && i == my_steps - 1)
+      next_claim = __hip_atomic_fetch_add(sched + kSchedNext, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  };
+  if (my_steps == 0) claim_at(-1);
+  int t = wave;
+  for (int i = 0; i < (my_steps >> 1); ++i, t += 2 * kWaves) {
+    claim_at(2 * i);
+    step(t, buf_a, buf_b, ids_b, ids_a);
+    claim_at(2 * i + 1);
+    step(t + kWaves, buf_b, buf_a, ids_a, ids_b);
+  }
+  if (my_steps & 1) {
+    claim_at(my_steps - 1);
+    step(t, buf_a, buf_b, ids_b, ids_a);
   }
 
   // ---- merge the four waves' states -------------------------------------
+  __asm__ volatile("" ::"v"(next_claim));  // awaited here by every lane, not only in the branch
+  if (tid == 0) s_unit[slot ^ 1] = q_begin + next_claim;
   float l_tot = xor32_sum(xor16_sum(l_run));
   __syncthreads();  // every wave is done with its V^T tile; publishes the claim
   // the next unit's Q, page ids and first K/V step load during this merge;
@@ -369,8 +413,10 @@ hipError_t launch_decode_d(const AttnArgs& a, bool paged, int grid, hipStream_t 
     decode_kernel<D, kRagged><<<grid, kThreads, 0, stream>>>(a);
   else if (a.page_shift >= 4)
     decode_kernel<D, kPagedUniform><<<grid, kThreads, 0, stream>>>(a);
-  else
+  else if (a.page_shift >= 0)
     decode_kernel<D, kPagedLane><<<grid, kThreads, 0, stream>>>(a);
+  else
+    decode_kernel<D, kPagedLaneDiv><<<grid, kThreads, 0, stream>>>(a);
   return hipGetLastError();
 }
 

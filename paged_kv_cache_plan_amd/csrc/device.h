@@ -19,6 +19,11 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4 ld16(const uint16_t* p) {
   return *reinterpret_cast<const u32x4*>(p);
 }
+// A streaming load of data read once (nontemporal: it does not displace
+// cached data that is read again).
+__device__ __forceinline__ u32x4 ld16_stream(const uint16_t* p) {
+  return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p));
+}
 __device__ __forceinline__ void st16(uint16_t* p, u32x4 v) { *reinterpret_cast<u32x4*>(p) = v; }
 __device__ __forceinline__ bf16x8 as_bf16x8(u32x4 v) { return __builtin_bit_cast(bf16x8, v); }
 
