@@ -202,7 +202,7 @@ constexpr int32_t kMixedMagic = 0x4d414b50;  // "PKAM"
 // bytes per ns per compute unit and kDecodeBytePerNs in all.
 constexpr double kPrefillFlopPerCuNs = 3500.0;
 constexpr double kDecodeBytePerCuNs = 30.0;
-constexpr double kDecodeBytePerNs = 5800.0;
+constexpr double kDecodeBytePerNs = 6300.0;
 
 struct MixedPlan {
   bool mixed = false;      // false: `single` is the whole plan

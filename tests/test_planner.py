@@ -179,7 +179,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
 
 # Compute-unit split of a mixed batch (planner.h: rates in flop and bytes per
 # ns, per compute unit, and the decode total).
-PREFILL_FLOP_PER_CU_NS, DECODE_BYTE_PER_CU_NS, DECODE_BYTE_PER_NS = 3500.0, 30.0, 5800.0
+PREFILL_FLOP_PER_CU_NS, DECODE_BYTE_PER_CU_NS, DECODE_BYTE_PER_NS = 3500.0, 30.0, 6300.0
 
 
 def restate_mixed_cus(flop, nbytes, num_cus=NUM_CUS, step=NUM_XCDS):
@@ -581,8 +581,8 @@ def test_mixed_named_workload_split():
 def test_mixed_cu_split_extremes():
     assert restate_mixed_cus(1e12, 0.0) == NUM_CUS - NUM_XCDS        # decode has nothing to do
     # prefill has nothing to do: decode gets the units it can use (its total
-    # rate saturates at 5800 / 30 = 193.3 units), ties go to prefill
-    assert restate_mixed_cus(0.0, 1e9) == 56
+    # rate saturates at 6300 / 30 = 210 units), ties go to prefill
+    assert restate_mixed_cus(0.0, 1e9) == 40
     p = restate_mixed_cus(4.0e11, 2.6e9)
     assert NUM_XCDS < p < NUM_CUS - NUM_XCDS
 
