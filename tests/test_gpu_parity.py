@@ -130,6 +130,34 @@ def test_decode_page_sizes_and_groups(ps, D, Hq, Hkv):
         compare(o, lse, *oracle_paged(w), f"decode ps={ps} D={D} G={Hq // Hkv} split={split}")
 
 
+# KV lengths around the decode kernel's step boundaries: 32 keys per step,
+# four waves taking steps in turn, steps run in pairs plus an odd last one,
+# so these give every wave 0..3 steps, odd and even counts, and partial steps
+_STEP_EDGES = [1, 2, 31, 32, 33, 63, 64, 65, 127, 128, 129, 160, 161, 255, 256, 257, 288, 289, 511, 512, 513]
+
+
+@pytest.mark.parametrize("ps", [1, 3, 4, 16, 32])
+def test_decode_step_boundaries(ps):
+    """Every K/V load of a decode step is issued unconditionally (keys past
+    the unit's end are clamped to its last row and masked), so lengths at and
+    around the step and pair boundaries must read no slot past kv_len: the
+    unused tails of the last pages are NaN-poisoned."""
+    w = W.build(f"dec_edges_ps{ps}", 70 + ps, [1] * len(_STEP_EDGES), _STEP_EDGES, 16, 4, 128, ps, causal=True,
+                pool_slack=0.1)
+    for split in (True, False):
+        o, lse, info = run_paged(w, disable_split_kv=not split)
+        assert info["kernel"] == pka.PKA_KERNEL_DECODE
+        compare(o, lse, *oracle_paged(w), f"decode step edges ps={ps} split={split}")
+
+
+def test_decode_step_boundaries_ragged():
+    w = W.build("dec_edges_ragged", 79, [1] * len(_STEP_EDGES), _STEP_EDGES, 16, 4, 128, 1, causal=True,
+                ragged=True, poison=False)
+    o, lse, info = run_ragged(w)
+    assert info["kernel"] == pka.PKA_KERNEL_DECODE
+    compare(o, lse, *oracle_paged(w), "decode step edges ragged")
+
+
 def test_decode_ragged():
     w = W.build("dec_ragged", 61, [1] * 9, [1, 5, 33, 64, 65, 700, 1500, 2, 2049], 16, 4, 128, 1, causal=True,
                 ragged=True, poison=False)
