@@ -4,10 +4,18 @@
 // query heads that share KV head hk are processed together so each K/V byte
 // is read from HBM once.  The launch is persistent: one workgroup per
 // resident slot takes units, longest first, from one queue and starts
-// loading its next unit while it merges and writes the current one.  The four waves take
-// interleaved 32-key steps of the range and keep independent online-softmax
-// states, merged through LDS at the end (the recursive-attention identity:
-// FlashInfer documentation, "Attention States and Recursive Attention").
+// loading its next unit while it merges and writes the current one.  The
+// four waves take interleaved 32-key steps of the range and keep independent
+// online-softmax states, merged through LDS at the end (the
+// recursive-attention identity: FlashInfer documentation, "Attention States
+// and Recursive Attention").
+//
+// Loads run two steps ahead of the math: a step issues the page ids of the
+// step after next, then the K/V rows of the next step (nontemporal: each
+// byte is read once), then computes on its own rows, which arrived during
+// the previous step.  Every load is unconditional (keys past a unit's end
+// read its last row and are masked), so the compiler's wait counts stay
+// exact and a step never waits for the loads queued behind its own.
 //
 // Per 32-key step of one wave:
 //   K        loaded from global straight into the A operand of
