@@ -91,13 +91,16 @@ enum MergeField : int {
 // whose grid does not depend on the batch can be replayed after the image
 // has been replaced by another batch's.  Queue q owns units [begin, end) of the
 // unit array; a worker takes the next unit with an atomic increment of the
-// queue's counter.  The last worker of a queue to finish sets both counters
-// back to zero, so the next run of the plan starts from a clean state without
-// a clearing launch.  One 64-word record per queue; the two counters sit on
-// their own 128-byte line, apart from the read-only fields.
+// queue's counter.  Decode: the last worker of the queue to finish sets both
+// counters back to zero.  Prefill: a worker whose queue is empty goes on to
+// the other queues, and the launch's last worker to finish (counted in queue
+// 0's done counter) sets every queue's counters back to zero.  Either way the
+// next run of the plan starts from a clean state without a clearing launch.
+// One 64-word record per queue; the two counters sit on their own 128-byte
+// line, apart from the read-only fields.
 enum SchedField : int {
   kSchedNext = 0,     // counter: units taken from this queue
-  kSchedDone = 1,     // counter: workers that found the queue empty
+  kSchedDone = 1,     // counter: workers done (prefill: of the launch, on queue 0)
   kSchedBegin = 32,
   kSchedEnd,
   kSchedWorkers,      // workers serving this queue
@@ -113,6 +116,7 @@ constexpr int kDecodeMaxGroup = 16;     // decode kernel holds up to 16 query he
 constexpr int kDecodeWgPerCu = 2;       // resident decode workgroups per CU (persistent launch)
 constexpr int kMergeGrid = 1024;        // split-merge workgroups of a batch-independent launch
 constexpr int kQueueWindow = 2;         // prefill queue: groups per longest-first window
+constexpr int kQueueTailSlots = 2;      // prefill queue: tail run longest-first, per worker slot
 
 constexpr uint32_t kFlagDisableSplit = 0x1u;
 constexpr uint32_t kFlagOutFp32 = 0x2u;

@@ -5,7 +5,8 @@
 // D=128 and 4 waves (128 rows) at D=64.  Packed row p of a request is token
 // p / G and query head hk * G + p % G, so the G query heads that share a KV
 // head share every K/V tile the workgroup loads.  The launch is persistent:
-// one workgroup per resident slot, each taking units from its XCD's queue.
+// one workgroup per resident slot, each taking units from its XCD's queue
+// and, once that is empty, from the other queues.
 //
 // PageAttention is block-sparse attention with page_size-wide blocks
 // (FlashInfer 0.2 release blog, "flexible block sparsity and vector
@@ -123,16 +124,33 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
   constexpr int NID = (one_page || pair_ids) ? 1 : KPT;
   constexpr bool pow2 = MODE != kKvPagedAny;
 
-  // Persistent: take units from this worker's queue until it runs dry.  The
-  // next unit is claimed during the current unit's last tile, and its Q and
-  // first K/V tile are in flight while the current unit writes its output.
+  // Persistent: the next unit is claimed during the current unit's last
+  // tile, and its Q and first K/V tile are in flight while the current unit
+  // writes its output.
   const PlanView pv = plan_view(a.ws);
-  int32_t* sched = pv.sched + (blockIdx.x % pv.num_queues) * kSchedWords;
-  const int q_begin = sched[kSchedBegin], q_end = sched[kSchedEnd];
+  // A worker serves its own queue (one per XCD, whose units share K/V in
+  // that XCD's L2) and, once it is empty, the other queues in turn, so that
+  // no worker idles while units remain anywhere.  A claim gives a unit
+  // index, or -1 once every queue has been found empty.
+  const int n_queues = pv.num_queues;
+  int q_cur = blockIdx.x % n_queues;  // (thread 0 only)
+  int q_left = n_queues;
   auto claim = [&](int slot) {
-    if (tid == 0)
-      s_unit[slot] = q_begin + __hip_atomic_fetch_add(sched + kSchedNext, 1, __ATOMIC_RELAXED,
-                                                      __HIP_MEMORY_SCOPE_AGENT);
+    if (tid == 0) {
+      int u = -1;
+      while (q_left > 0) {
+        int32_t* sq = pv.sched + q_cur * kSchedWords;
+        const int v = sq[kSchedBegin] + __hip_atomic_fetch_add(sq + kSchedNext, 1, __ATOMIC_RELAXED,
+                                                               __HIP_MEMORY_SCOPE_AGENT);
+        if (v < sq[kSchedEnd]) {
+          u = v;
+          break;
+        }
+        --q_left;
+        q_cur = q_cur + 1 == n_queues ? 0 : q_cur + 1;
+      }
+      s_unit[slot] = u;
+    }
   };
 
   // ---- per-unit lane facts -----------------------------------------------
@@ -271,12 +289,12 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
   int ui = __builtin_amdgcn_readfirstlane(s_unit[0]);
   int slot = 0;
   UnitInfo U{};
-  if (ui < q_end) {
+  if (ui >= 0) {
     U = load_unit(pv, ui);
     start_unit(U);
   }
 
-  while (ui < q_end) {
+  while (ui >= 0) {
     const int lim = lane_of(U).lim;
     const int wrow0 = U.row_begin + wave * 32;
     const bool wave_active = wrow0 < U.row_end;
@@ -402,7 +420,7 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
     // unit ago, before barriers every thread has since passed.
     const int un = __builtin_amdgcn_readfirstlane(s_unit[slot ^ 1]);
     const UnitInfo Uc = U;
-    if (un < q_end) {
+    if (un >= 0) {
       U = load_unit(pv, un);
       start_unit(U);
     }
@@ -463,13 +481,16 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
     }
   }
 
-  // The last worker of the queue to get here resets its counters for the
-  // next run; acq_rel orders every worker's final take before the reset.
+  // Workers take units from every queue, so the launch's last worker to get
+  // here (counted on queue 0's record) resets every queue's counter for the
+  // next run; acq_rel orders every worker's final takes before the reset.
   if (tid == 0) {
-    const int done = __hip_atomic_fetch_add(sched + kSchedDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-    if (done == sched[kSchedWorkers] - 1) {
-      __hip_atomic_store(sched + kSchedNext, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(sched + kSchedDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    int32_t* s0 = pv.sched;
+    const int done = __hip_atomic_fetch_add(s0 + kSchedDone, 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    if (done == static_cast<int>(gridDim.x) - 1) {
+      for (int q = 0; q < n_queues; ++q)
+        __hip_atomic_store(pv.sched + q * kSchedWords + kSchedNext, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(s0 + kSchedDone, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 }
