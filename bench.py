@@ -1,7 +1,7 @@
 #!/usr/bin/env python3
 """Benchmark of paged-KV batch attention on one MI355X.
 
-    python bench.py [--steps K] [--warmup W] [--only NAME] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--warm-ms MS] [--only NAME] [--no-cpu-baseline]
 
 A step is one run of the planned batch (every kernel the plan launches:
 attention, and the split-KV merge when the plan split any KV) over inputs
@@ -19,7 +19,10 @@ and batch decode (HBM-bound) under "workloads".
 Throughput uses algorithmic work only: prefill flops = 4 D Hq (visible
 query-key pairs); decode bytes = every valid K/V row once + q + o + lse +
 page ids.  Two input copies alternate between steps so that no step finds
-its K/V left in the 256 MB last-level cache by the previous one.
+its K/V left in the 256 MB last-level cache by the previous one.  Before the
+timed steps, each workload runs at least W launches and at least --warm-ms
+(default 300) of back-to-back launches: the GPU's clocks ramp up over the
+first ~100 ms under load, and the timed steps measure the steady state.
 """
 from __future__ import annotations
 
@@ -79,14 +82,25 @@ def make_plan(w, dev, ragged=False):
     return plan, plan_ms
 
 
+WARM_MS = 300.0  # minimum back-to-back warm-up per workload (the GPU's clocks ramp up under load)
+
+
 def time_launches(launch, steps, warmup):
-    """Warm up, then time exactly `steps` launches bracketed by synchronisation.
-    Returns (total ms, per-launch ms list) from HIP events recorded on the
-    stream the library launches on (torch's current stream)."""
+    """Warm up (at least `warmup` launches and WARM_MS of back-to-back
+    launches, so that the timed launches run at steady-state clocks), then
+    time exactly `steps` launches bracketed by synchronisation.  Returns
+    (total ms, per-launch ms list) from HIP events recorded on the stream the
+    library launches on (torch's current stream)."""
     import torch
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    t0, i = time.perf_counter(), warmup
+    while (time.perf_counter() - t0) * 1e3 < WARM_MS:
+        for _ in range(4):
+            launch(i)
+            i += 1
+        torch.cuda.synchronize()
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     start.record()
@@ -292,16 +306,20 @@ def load_traffic():
 
 
 def main():
+    global WARM_MS
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--warm-ms", type=float, default=WARM_MS,
+                    help="minimum back-to-back warm-up per workload before timing (ms)")
     ap.add_argument("--only", default=None,
                     help="run one workload: c2_paged, c2_ragged, c3, c4, c5, append, mixed (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
+    WARM_MS = args.warm_ms
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(see the sharding notes); run with --gpus 1", file=sys.stderr)
