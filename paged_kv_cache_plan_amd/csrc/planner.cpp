@@ -256,6 +256,17 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
       std::stable_sort(q.begin() + window_start[x], q.end(),
                        [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
     }
+    // The last units a queue hands out (twice as many as it can have
+    // workers) run longest-first across groups, so that its workers finish
+    // together; this costs some L2 reuse at the end.
+    const int64_t slots_per_queue =
+        std::max<int64_t>(1, int64_t(std::max(1, in.num_cus)) * prefill_wg_per_cu(in.head_dim) / X);
+    const size_t tail = static_cast<size_t>(kQueueTailSlots * slots_per_queue);
+    for (int x = 0; x < X; ++x) {
+      std::vector<Unit>& q = queue[x];
+      const size_t t0 = q.size() > tail ? q.size() - tail : 0;
+      std::stable_sort(q.begin() + t0, q.end(), [](const Unit& a, const Unit& b) { return a.cost > b.cost; });
+    }
     std::vector<Unit> out;
     out.reserve(units.size());
     for (int x = 0; x < X; ++x) {

@@ -116,6 +116,7 @@ constexpr int kDecodeMaxGroup = 16;     // decode kernel holds up to 16 query he
 constexpr int kDecodeWgPerCu = 2;       // resident decode workgroups per CU (persistent launch)
 constexpr int kMergeGrid = 1024;        // split-merge workgroups of a batch-independent launch
 constexpr int kQueueWindow = 2;         // prefill queue: groups per longest-first window
+constexpr int kQueueTailSlots = 2;      // prefill queue: tail run longest-first, per worker slot
 
 constexpr uint32_t kFlagDisableSplit = 0x1u;
 constexpr uint32_t kFlagOutFp32 = 0x2u;

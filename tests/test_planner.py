@@ -32,7 +32,7 @@ def block_rows(D):
 
 def wg_per_cu(D):
     return 1 if D == 128 else 2
-NUM_CUS, NUM_XCDS, QUEUE_WINDOW = 256, 8, 2
+NUM_CUS, NUM_XCDS, QUEUE_WINDOW, QUEUE_TAIL_SLOTS = 256, 8, 2, 2
 UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 16, 8, 8
 
 
@@ -133,10 +133,16 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             queues[x].append(units[grps[g][1]:grps[g][2]])
         # windows of QUEUE_WINDOW groups, units longest-first inside a window
         # (ties: group order, then planning order)
-        queues = [[u[0] for i in range(0, len(gs), QUEUE_WINDOW)
+        queues = [[u for i in range(0, len(gs), QUEUE_WINDOW)
                    for u in sorted([v for g in gs[i:i + QUEUE_WINDOW] for v in g],
                                    key=lambda v: -v[1])]
                   for gs in queues]
+        # the last QUEUE_TAIL_SLOTS units per worker slot of a queue run
+        # longest-first across its groups (stable: ties keep queue order)
+        tail = QUEUE_TAIL_SLOTS * max(1, num_cus * wg_per_cu(D) // NUM_XCDS)
+        queues = [q[:max(0, len(q) - tail)] + sorted(q[max(0, len(q) - tail):], key=lambda v: -v[1])
+                  for q in queues]
+        queues = [[u[0] for u in q] for q in queues]
         order = []
         for q in queues:
             order += q
