@@ -103,8 +103,8 @@ typedef struct pka_plan_info {
   int64_t total_kv;         /* sum of kv_len over the batch                                 */
   int64_t int_ws_bytes;     /* bytes of the int workspace image the plan uploads            */
   int64_t float_ws_bytes;   /* bytes of float workspace the runs need                       */
-  int32_t num_workers;      /* workgroups of the attention launch (prefill: persistent,
-                               each takes units from a queue until it is empty)            */
+  int32_t num_workers;      /* workgroups of the persistent attention launch (prefill: each
+                               takes units from its XCD's queue, then from the others)     */
   int32_t num_queues;       /* unit queues: one per XCD for prefill, one for decode          */
   int32_t prefill_cus;      /* mixed batch: compute units the prefill launch is sized for    */
   int32_t decode_cus;       /* mixed batch: compute units the decode launch is sized for     */
