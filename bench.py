@@ -267,6 +267,52 @@ def bench_mixed(w, dev, steps, warmup, copies=2):
     return res
 
 
+def bench_cascade(w, dev, steps, warmup, copies=2):
+    """Batch decode over a long shared prefix, two ways, each timed with HIP
+    events on the caller's stream: (a) one flat decode plan whose page table
+    lists the prefix in every request; (b) the two-level cascade (level 0:
+    all queries over the prefix, read once; level 1: each request over its
+    suffix; then the state merge).  decode_bytes is what the flat form must
+    read; cascade_unique_bytes the K/V the cascade reads once."""
+    import torch
+    import paged_kv_cache_plan_amd as pka
+    flat = pka.Plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.num_qo_heads, w.num_kv_heads,
+                    w.head_dim, w.page_size, causal=w.causal, sm_scale=w.sm_scale, num_pages=w.num_pages,
+                    device=dev)
+    t0 = time.perf_counter()
+    casc = pka.Cascade(w.notes["levels"], w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                       causal=w.causal, sm_scale=w.sm_scale, num_pages=w.num_pages, device=dev)
+    plan_ms = (time.perf_counter() - t0) * 1e3
+    qs = [w.q] + [w.q.clone() for _ in range(copies - 1)]
+    pools = [w.paged_kv] + [w.paged_kv.clone() for _ in range(copies - 1)]
+    o = torch.empty((w.total_q, w.num_qo_heads, w.head_dim), dtype=torch.bfloat16, device=dev)
+    lse = torch.empty((w.total_q, w.num_qo_heads), dtype=torch.float32, device=dev)
+
+    def run_flat(i):
+        flat.run(qs[i % copies], pools[i % copies], o, lse)
+
+    def run_cascade(i):
+        casc.run(qs[i % copies], pools[i % copies])
+
+    res = {"kernel": "cascade", "plan_ms": plan_ms, "requests": w.batch, "prefix": w.notes["prefix"],
+           "levels": len(w.notes["levels"])}
+    for name, fn in (("flat", run_flat), ("cascade", run_cascade)):
+        _, per = time_launches(fn, steps, warmup)
+        res[f"{name}_ms_avg"] = sum(per) / len(per)
+        res[f"{name}_ms_median"] = sorted(per)[len(per) // 2]
+    flat.close()
+    casc.close()
+    b = decode_bytes(w)
+    row = 4.0 * w.num_kv_heads * w.head_dim
+    unique = row * (w.notes["prefix"] + sum(w.notes["suffixes"]))
+    res.update({"decode_bytes": b, "cascade_unique_bytes": unique,
+                "flat_GB_per_s": b / (res["flat_ms_avg"] * 1e-3) / 1e9,
+                "speedup": res["flat_ms_avg"] / res["cascade_ms_avg"], "ms_per_step": res["cascade_ms_avg"]})
+    del qs, pools, o, lse
+    torch.cuda.empty_cache()
+    return res
+
+
 def cpu_baseline(w, budget_s=10.0):
     """The CPU fp64 oracle, as it stands, on a bounded sample of the headline
     workload (the same inputs the GPU was timed on, copied to the host):
@@ -314,7 +360,7 @@ def main():
     ap.add_argument("--warm-ms", type=float, default=WARM_MS,
                     help="minimum back-to-back warm-up per workload before timing (ms)")
     ap.add_argument("--only", default=None,
-                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5, append, mixed (profiling runs)")
+                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5, append, mixed, cascade (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -386,6 +432,12 @@ def main():
         results["mixed_batch"] = bench_mixed(wm, dev, args.steps, args.warmup)
         print(f"# mixed: {results['mixed_batch']}", file=sys.stderr, flush=True)
         del wm
+        torch.cuda.empty_cache()
+    if want("cascade"):
+        wc = W.shared_prefix_decode(device=dev)
+        results["shared_prefix_decode"] = bench_cascade(wc, dev, args.steps, args.warmup)
+        print(f"# cascade: {results['shared_prefix_decode']}", file=sys.stderr, flush=True)
+        del wc
         torch.cuda.empty_cache()
 
     if sel is not None:

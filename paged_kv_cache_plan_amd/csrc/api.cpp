@@ -45,6 +45,7 @@ int env_int(const char* name) {
 // two, the prefill one first.
 struct PartLaunch {
   int32_t kernel, num_workers, num_merge;
+  int32_t merge_slices;  // workgroup slices of its largest merge group
   int32_t off_words;  // its image inside the int workspace
   size_t float_off;   // its partial states inside the float workspace (bytes)
 };
@@ -191,12 +192,13 @@ int upload(pka_plan* p, const Planned& pl, int32_t batch, int32_t nnz, hipStream
   if (pl.mp.mixed) {
     const pka::MixedPlan& mp = pl.mp;
     p->num_parts = 2;
-    p->parts[0] = {mp.prefill.kernel, mp.prefill.num_workers, mp.prefill.num_merge, mp.off_prefill, 0};
-    p->parts[1] = {mp.decode.kernel, mp.decode.num_workers, mp.decode.num_merge, mp.off_decode,
-                   mp.float_off_decode};
+    p->parts[0] = {mp.prefill.kernel, mp.prefill.num_workers, mp.prefill.num_merge,
+                   mp.prefill.image[pka::kHdrMergeSlices], mp.off_prefill, 0};
+    p->parts[1] = {mp.decode.kernel, mp.decode.num_workers, mp.decode.num_merge,
+                   mp.decode.image[pka::kHdrMergeSlices], mp.off_decode, mp.float_off_decode};
   } else {
     p->num_parts = 1;
-    p->parts[0] = {res.kernel, res.num_workers, res.num_merge, 0, 0};
+    p->parts[0] = {res.kernel, res.num_workers, res.num_merge, res.image[pka::kHdrMergeSlices], 0, 0};
   }
   return PKA_OK;
 }
@@ -263,7 +265,10 @@ int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const voi
     m.num_qo_heads = p->num_qo_heads;
     m.group = p->group;
     m.out_fp32 = a.out_fp32;
-    e = pka::launch_merge(m, p->head_dim, stable ? pka::kMergeGrid : part.num_merge, stream);
+    // one workgroup per (slice, group), up to a cap (the kernel is grid-stride)
+    const int64_t pairs = int64_t(part.num_merge) * std::max(1, part.merge_slices);
+    const int grid = stable ? pka::kMergeGrid : static_cast<int>(std::min<int64_t>(pairs, 8 * pka::kMergeGrid));
+    e = pka::launch_merge(m, p->head_dim, grid, stream);
     if (e != hipSuccess) return hip_error("merge launch", e);
   }
   return PKA_OK;

@@ -74,7 +74,8 @@ struct PlanView {
   int32_t* sched;
   int32_t num_queues;
   int32_t num_merge;
-  int32_t partial_lse;  // float index of the partial lse in the float workspace
+  int32_t merge_slices;  // workgroup slices of the largest merge group
+  int32_t partial_lse;   // float index of the partial lse in the float workspace
 };
 __device__ __forceinline__ PlanView plan_view(const int32_t* ws) {
   PlanView v;
@@ -85,6 +86,7 @@ __device__ __forceinline__ PlanView plan_view(const int32_t* ws) {
   v.sched = const_cast<int32_t*>(ws) + ws[kHdrOffSched];
   v.num_queues = ws[kHdrNumQueues];
   v.num_merge = ws[kHdrNumMerge];
+  v.merge_slices = ws[kHdrMergeSlices];
   v.partial_lse = ws[kHdrPartialLse];
   return v;
 }

@@ -30,44 +30,80 @@ __device__ __forceinline__ void store4(void* out, int64_t idx, f32x4 v, bool fp3
   }
 }
 
-// Split groups, one per workgroup, grid-stride: rows [row0, row1) of
-// (request, kv head).  The group list and its length come from the plan
-// image, so the launch does not depend on the batch.
+// Split groups: rows [row0, row1) of (request, kv head), each row with S
+// partial states.  A group's items (row, 4 d) are cut into whole blocks of
+// kMergeBlock items and spread over up to merge_slices workgroups (the plan
+// gives the slice count of its largest group), and workgroups take
+// (slice, group) pairs grid-stride, slice-major: a few large groups (a long
+// prefill split over many chunks) spread over the GPU as well as many small
+// ones (decode).  Each thread keeps eight states' loads in flight.  The group
+// list and the counts come from the plan image, so the launch does not depend
+// on the batch.
+static_assert(kThreads == kMergeBlock, "one item per thread per block");
+
 template <int D>
 __global__ __launch_bounds__(kThreads) void merge_split_kernel(MergeArgs a) {
   constexpr int C4 = D / 4;
+  constexpr int kBatch = 8;  // states per batch of loads
   const PlanView pv = plan_view(a.ws);
   const float* part_lse = a.part_o + pv.partial_lse;
-  for (int gi = blockIdx.x; gi < pv.num_merge; gi += gridDim.x) {
-  const int32_t* g = pv.merge + static_cast<int64_t>(gi) * 8;
-  const int r = g[0], hk = g[1], row0 = g[2], row1 = g[3], pbase = g[4], S = g[5];
-  const int nrows = row1 - row0;
-  const int qo_begin = pv.req[static_cast<int64_t>(r) * 8];
   const int G = a.group, Hq = a.num_qo_heads;
-  for (int it = threadIdx.x; it < nrows * C4; it += kThreads) {
-    const int row = it / C4, c4 = it - row * C4;
-    float M = -INFINITY;
-    for (int s = 0; s < S; ++s) M = fmaxf(M, part_lse[pbase + s * nrows + row]);
-    float W = 0.f;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-    if (M != -INFINITY) {
-      for (int s = 0; s < S; ++s) {
-        const int64_t prow = pbase + s * nrows + row;
-        const float w = fast_exp2(part_lse[prow] - M);
-        if (w > 0.f) {
-          W += w;
-          acc += w * *reinterpret_cast<const f32x4*>(a.part_o + prow * D + 4 * c4);
+  const int n_groups = pv.num_merge, n_sl = pv.merge_slices;
+  for (int v = blockIdx.x; v < n_groups * n_sl; v += gridDim.x) {
+    const int slice = v / n_groups, gi = v - slice * n_groups;
+    const int32_t* g = pv.merge + static_cast<int64_t>(gi) * 8;
+    const int r = g[0], hk = g[1], row0 = g[2], row1 = g[3], pbase = g[4], S = g[5];
+    const int nrows = row1 - row0;
+    const int items = nrows * C4;
+    const int blocks = (items + kMergeBlock - 1) / kMergeBlock;
+    const int g_sl = min(n_sl, blocks);  // this group's slices
+    if (slice >= g_sl) continue;
+    const int per = (blocks + g_sl - 1) / g_sl * kMergeBlock;
+    const int lo = slice * per, hi = min(items, lo + per);
+    const int qo_begin = pv.req[static_cast<int64_t>(r) * 8];
+    for (int it = lo + threadIdx.x; it < hi; it += kThreads) {
+      const int row = it / C4, c4 = it - row * C4;
+      const int64_t base = static_cast<int64_t>(pbase) + row;  // partial row of state s: base + s * nrows
+      float M = -INFINITY;
+      for (int s0 = 0; s0 < S; s0 += kBatch) {
+        float l[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j)
+          l[j] = s0 + j < S ? part_lse[base + static_cast<int64_t>(s0 + j) * nrows] : -INFINITY;
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) M = fmaxf(M, l[j]);
+      }
+      float W = 0.f;
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+      if (M != -INFINITY) {
+        // an empty state (lse = -inf) weighs 0 and holds o = 0; states past S
+        // read state s0's (finite) row with weight 0
+        for (int s0 = 0; s0 < S; s0 += kBatch) {
+          float l[kBatch];
+          f32x4 x[kBatch];
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) {
+            const bool ok = s0 + j < S;
+            const int64_t prow = base + static_cast<int64_t>(ok ? s0 + j : s0) * nrows;
+            l[j] = ok ? part_lse[prow] : -INFINITY;
+            x[j] = *reinterpret_cast<const f32x4*>(a.part_o + prow * D + 4 * c4);
+          }
+#pragma unroll
+          for (int j = 0; j < kBatch; ++j) {
+            const float w = fast_exp2(l[j] - M);
+            W += w;
+            acc += w * x[j];
+          }
         }
       }
+      const bool seen = W > 0.f;
+      const float inv = seen ? 1.f / W : 0.f;
+      const int p = row0 + row;
+      const int tok = p / G;
+      const int64_t orow = static_cast<int64_t>(qo_begin + tok) * Hq + hk * G + (p - tok * G);
+      store4(a.o, orow * D + 4 * c4, acc * inv, a.out_fp32 != 0);
+      if (a.lse && c4 == 0) a.lse[orow] = seen ? M + __log2f(W) : -INFINITY;
     }
-    const bool seen = W > 0.f;
-    const float inv = seen ? 1.f / W : 0.f;
-    const int p = row0 + row;
-    const int tok = p / G;
-    const int64_t orow = static_cast<int64_t>(qo_begin + tok) * Hq + hk * G + (p - tok * G);
-    store4(a.o, orow * D + 4 * c4, acc * inv, a.out_fp32 != 0);
-    if (a.lse && c4 == 0) a.lse[orow] = seen ? M + __log2f(W) : -INFINITY;
-  }
   }
 }
 

@@ -163,6 +163,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
 
   std::vector<int32_t> merge;
   int64_t partial_rows = 0;
+  int32_t max_merge_rows = 0;
   bool any_split = false;
   for (const Block& b : blocks) {
     const int64_t n_split = (chunk > 0 && b.kv_hi > chunk) ? ceil_div(b.kv_hi, chunk) : 1;
@@ -175,6 +176,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
       if (partial_rows > (int64_t(1) << 30)) return fail(err, kUnsupported, "too many partial rows");
       merge.insert(merge.end(), {b.r, b.hk, b.row0, b.row1, static_cast<int32_t>(pbase),
                                  static_cast<int32_t>(n_split), 0, 0});
+      max_merge_rows = std::max(max_merge_rows, nrows);
     }
     for (int64_t s = 0; s < n_split; ++s) {
       Unit u{};
@@ -316,6 +318,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   im[kHdrOffSched] = off_sched;
   im[kHdrNumQueues] = n_queues;
   im[kHdrNumWorkers] = n_workers;
+  im[kHdrMergeSlices] = merge_slices(max_merge_rows, in.head_dim);
   for (int32_t q = 0; q < n_queues; ++q) {
     int32_t* rec = im + off_sched + int64_t(q) * kSchedWords;
     rec[kSchedBegin] = queue_begin[q];

@@ -39,6 +39,7 @@ enum HeaderField : int {
   kHdrNumQueues,    // number of unit queues
   kHdrNumWorkers,   // workgroups of the attention launch
   kHdrPartialLse,   // float index of the partial lse section in the float workspace
+  kHdrMergeSlices,  // slices the split merge cuts the largest merge group into (>= 1)
   kHdrWords = 32
 };
 constexpr int32_t kMagic = 0x31414b50;  // "PKA1"
@@ -115,6 +116,18 @@ constexpr int kDecodeTileKeys = 32;     // keys per decode wave step
 constexpr int kDecodeMaxGroup = 16;     // decode kernel holds up to 16 query heads per KV head
 constexpr int kDecodeWgPerCu = 2;       // resident decode workgroups per CU (persistent launch)
 constexpr int kMergeGrid = 1024;        // split-merge workgroups of a batch-independent launch
+constexpr int kMergeBlock = 256;        // split merge: items (row, 4 d) per workgroup pass
+constexpr int kMergeSlicesMax = 32;     // split merge: at most this many workgroups per group
+
+// Slices of a merge group of `rows` rows: whole kMergeBlock blocks of its
+// rows * head_dim / 4 items, at most kMergeSlicesMax.
+constexpr int32_t merge_slices(int64_t rows, int32_t head_dim) {
+  return static_cast<int32_t>(
+      rows <= 0 ? 1
+                : ((rows * (head_dim / 4) + kMergeBlock - 1) / kMergeBlock < kMergeSlicesMax
+                       ? (rows * (head_dim / 4) + kMergeBlock - 1) / kMergeBlock
+                       : kMergeSlicesMax));
+}
 constexpr int kQueueWindow = 2;         // prefill queue: groups per longest-first window
 constexpr int kQueueTailSlots = 2;      // prefill queue: tail run longest-first, per worker slot
 

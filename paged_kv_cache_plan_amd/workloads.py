@@ -280,6 +280,57 @@ def p5_shape(seed=6, batch=4, max_len=700, **kw) -> Workload:
                  pool_slack=0.25, gen=gen, **kw)
 
 
+def shared_prefix_decode(seed=10, batch=64, prefix=16384, suffix_range=(128, 1024), heads=32, kv_heads=8,
+                         head_dim=128, page_size=16, device="cpu") -> Workload:
+    """Batch decode over one long shared prefix (cascade inference): every
+    request's keys are the same `prefix` tokens (a multiple of page_size)
+    followed by its own suffix of S_r ~ U{...} tokens, one query token each.
+
+    The flat page table lists the prefix pages in every request.
+    ``notes["levels"]`` holds the same keys in two-level cascade form: level 0
+    is one group of all requests over the prefix pages, level 1 one group per
+    request over its suffix pages.  Draw order: suffix lengths -> page
+    permutation -> Q -> pool.  Unused slots of the last suffix pages are
+    poisoned."""
+    ps = page_size
+    if prefix % ps:
+        raise ValueError("prefix must be a multiple of page_size")
+    gen = torch.Generator("cpu").manual_seed(seed)
+    suf = _uniform_int(gen, suffix_range[0], suffix_range[1], batch)
+    n_pre = prefix // ps
+    n_suf = [(s + ps - 1) // ps for s in suf]
+    num_pages = n_pre + sum(n_suf)
+    perm = torch.randperm(num_pages, generator=gen).to(torch.int32)
+    pre_ids = perm[:n_pre]
+    suf_ids, pos = [], n_pre
+    for n in n_suf:
+        suf_ids.append(perm[pos:pos + n])
+        pos += n
+    last = torch.tensor([s - (n - 1) * ps for s, n in zip(suf, n_suf)], dtype=torch.int32)
+    kv_indices = torch.cat([torch.cat([pre_ids, ids]) for ids in suf_ids])
+    kv_indptr = torch.tensor([0] + list(torch.tensor([n_pre + n for n in n_suf]).cumsum(0).tolist()),
+                             dtype=torch.int32)
+    qo_indptr = torch.arange(batch + 1, dtype=torch.int32)
+    dev = torch.device(device)
+    vgen = gen if dev.type == "cpu" else torch.Generator(device=dev).manual_seed(seed)
+    q = _randn_bf16((batch, heads, head_dim), vgen)
+    paged_kv = _randn_bf16((num_pages, 2, ps, kv_heads, head_dim), vgen)
+    kv_lens = [prefix + s for s in suf]
+    _poison(paged_kv, kv_indptr, kv_indices, last, ps)
+    levels = [
+        (torch.tensor([0, batch], dtype=torch.int32), torch.tensor([0, n_pre], dtype=torch.int32), pre_ids.clone(),
+         torch.tensor([ps], dtype=torch.int32)),
+        (qo_indptr.clone(), torch.tensor([0] + list(torch.tensor(n_suf).cumsum(0).tolist()), dtype=torch.int32),
+         torch.cat(suf_ids), last.clone()),
+    ]
+    return Workload(
+        name="shared_prefix_decode", seed=seed, batch=batch, num_qo_heads=heads, num_kv_heads=kv_heads,
+        head_dim=head_dim, page_size=ps, causal=True, sm_scale=1.0 / math.sqrt(head_dim),
+        qo_lens=[1] * batch, kv_lens=kv_lens, qo_indptr=qo_indptr, kv_indptr=kv_indptr,
+        kv_indices=kv_indices, kv_last_page_len=last, num_pages=num_pages, q=q, paged_kv=paged_kv,
+        poisoned=True, notes={"levels": levels, "prefix": prefix, "suffixes": suf})
+
+
 WORKLOADS = {
     "tiny": tiny,
     "dense_vs_sparse": dense_vs_sparse,
@@ -288,6 +339,7 @@ WORKLOADS = {
     "batch_decode": batch_decode,
     "p5_shape": p5_shape,
     "mixed_batch": mixed_batch,
+    "shared_prefix_decode": shared_prefix_decode,
 }
 
 

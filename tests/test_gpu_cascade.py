@@ -106,3 +106,25 @@ def test_merge_states_levels():
     vo, so = pka.merge_states_levels(v.to(dev), s.to(dev), out_fp32=True)
     ro, rs = oracle.merge_states(v.permute(1, 0, 2, 3).double(), s.permute(1, 0, 2).double())
     compare(vo.cpu(), so.cpu(), ro, rs, "merge levels")
+
+
+def test_shared_prefix_decode_full_size():
+    """The benchmarked shared-prefix decode (64 requests over one 16384-token
+    prefix plus their own 128..1024-token suffixes, Hq=32, Hkv=8, D=128,
+    page_size=16), drawn on the GPU as bench.py draws it: the two-level
+    cascade and the flat decode plan both match the oracle on every row."""
+    from paged_kv_cache_plan_amd import workloads as W
+    from tests.gpu_common import oracle_paged, run_paged
+    dev = cuda()
+    w = W.shared_prefix_decode(device=dev)
+    c = pka.Cascade(w.notes["levels"], w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size, causal=True,
+                    sm_scale=w.sm_scale, num_pages=w.num_pages, device=dev)
+    o, lse = c.run(w.q, w.paged_kv)
+    torch.cuda.synchronize()
+    c.close()
+    fo, fl, info = run_paged(w)
+    assert info["kernel"] == pka.PKA_KERNEL_DECODE
+    w.q, w.paged_kv = w.q.cpu(), w.paged_kv.cpu()
+    ref_o, ref_l = oracle_paged(w)
+    compare(o.float().cpu(), lse.cpu(), ref_o, ref_l, "shared-prefix cascade")
+    compare(fo, fl, ref_o, ref_l, "shared-prefix flat")

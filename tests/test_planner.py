@@ -162,9 +162,12 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     total = off_idx + align(max(nnz, 1))
     img = [0] * total
     part_lse = _cdiv(partial * D * 4, 256) * 256 // 4
+    # slices of the largest merge group: whole 256-item blocks of rows * D / 4, at most 32
+    max_rows = max((m[3] - m[2] for m in merge), default=0)
+    merge_slices = 1 if max_rows == 0 else min(32, _cdiv(max_rows * (D // 4), 256))
     hdr = [0x31414b50, 1 if decode else 0, len(order), len(merge), B, nnz, off_units, off_req,
            off_merge, off_idx, partial, rows_per, chunk if any_split else 0, flags, off_sched, nq, workers,
-           part_lse]
+           part_lse, merge_slices]
     img[:len(hdr)] = hdr
     for q in range(nq):  # counters (words 0, 1) start at zero
         img[off_sched + 64 * q + 32: off_sched + 64 * q + 35] = [bounds[q], bounds[q + 1], per_queue]
