@@ -7,6 +7,7 @@
 // only enqueue kernels.  Errors become status codes plus a per-thread message.
 #include <hip/hip_runtime_api.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstdio>
 #include <cstdlib>
