@@ -191,6 +191,18 @@ def test_edge_cases():
     compare(o, lse, *oracle_paged(w), "edge")
 
 
+@pytest.mark.parametrize("ps", [1, 16])
+def test_decode_empty_kv(ps):
+    """Decode requests with no keys (kv_len 0) next to short ones: (0, -inf)
+    rows, and no load of the empty requests' (absent) pages."""
+    w = W.build(f"dec_empty_ps{ps}", 80 + ps, [1] * 6, [0, 1, 33, 0, 200, 0], 8, 2, 128, ps, causal=True,
+                pool_slack=0.2)
+    for split in (True, False):
+        o, lse, info = run_paged(w, disable_split_kv=not split)
+        assert info["kernel"] == pka.PKA_KERNEL_DECODE
+        compare(o, lse, *oracle_paged(w), f"decode empty kv ps={ps} split={split}")
+
+
 def test_plan_upload_bit_exact():
     w = W.gqa_append(batch=5, prefix_range=(10, 900), chunk_range=(1, 200))
     img, _ = pka.plan_host_image(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len,
