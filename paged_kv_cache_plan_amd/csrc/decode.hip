@@ -124,7 +124,7 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
 
   // Page ids of a step.
   struct IdsUniform { int s[2]; };
-  struct IdsLane { int k[2]; int v[8]; };
+  struct IdsLane { int key; };  // lane l: the page id of key k0 + (l % 32)
   struct IdsNone {};
   using Ids = typename std::conditional<MODE == kPagedUniform, IdsUniform,
                 typename std::conditional<LANE, IdsLane, IdsNone>::type>::type;
@@ -147,16 +147,10 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
       id.s[0] = pv.kv_indices[kv_base + (min(k0, last) >> pshift) + z];
       id.s[1] = pv.kv_indices[kv_base + (min(k0 + 16, last) >> pshift) + z];
     } else if constexpr (LANE) {
-#pragma unroll
-      for (int kb = 0; kb < 2; ++kb) {
-        const int key = min(k0 + 16 * kb + col, last);
-        id.k[kb] = pv.kv_indices[kv_base + page_of(key)];
-      }
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int key = min(k0 + v_key(j), last);
-        id.v[j] = pv.kv_indices[kv_base + page_of(key)];
-      }
+      // one id load per lane; the K and V rows' lanes fetch theirs from the
+      // lane that holds them (ds_bpermute) when the data loads are formed
+      const int key = min(k0 + (lane & 31), last);
+      id.key = pv.kv_indices[kv_base + page_of(key)];
     }
   };
   auto row_off = [&](int key, int pid) -> int64_t {  // element offset of the K row of `key`
@@ -176,7 +170,7 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
       const int key = min(k0 + 16 * kb + col, last);
       int pid = 0;
       if constexpr (MODE == kPagedUniform) pid = id.s[kb];
-      if constexpr (LANE) pid = id.k[kb];
+      if constexpr (LANE) pid = __builtin_amdgcn_ds_bpermute((16 * kb + col) * 4, id.key);
       const uint16_t* p = kb_ptr + row_off(key, pid) + 8 * g4;
 #pragma unroll
       for (int s = 0; s < DS; ++s) x.k[kb][s] = ld16_stream(p + 32 * s);
@@ -186,7 +180,7 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
       const int key = min(k0 + v_key(j), last);
       int pid = 0;
       if constexpr (MODE == kPagedUniform) pid = id.s[j >> 2];
-      if constexpr (LANE) pid = id.v[j];
+      if constexpr (LANE) pid = __builtin_amdgcn_ds_bpermute(v_key(j) * 4, id.key);
       x.v[j] = ld16_stream(vb_ptr + row_off(key, pid) + 8 * vc);  // lanes past the 4 V groups load and ignore
     }
   };
