@@ -360,7 +360,7 @@ def main():
     ap.add_argument("--warm-ms", type=float, default=WARM_MS,
                     help="minimum back-to-back warm-up per workload before timing (ms)")
     ap.add_argument("--only", default=None,
-                    help="run one workload: c2_paged, c2_ragged, c3, c4, c5, append, mixed, cascade (profiling runs)")
+                    help="run one workload: dense_vs_sparse_paged, dense_vs_sparse_ragged, gqa_append, long_causal, batch_decode, append, mixed, cascade (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
@@ -396,30 +396,30 @@ def main():
         return sel is None or sel == n
 
     w2 = None
-    if want("c2_paged") or want("c2_ragged"):
+    if want("dense_vs_sparse_paged") or want("dense_vs_sparse_ragged"):
         w2 = W.dense_vs_sparse(device=dev)
-        if want("c2_paged"):
-            results["dense_vs_sparse_paged_ps1"] = bench_workload("c2_paged", w2, dev, args.steps, args.warmup)
-            print(f"# c2 paged: {results['dense_vs_sparse_paged_ps1']}", file=sys.stderr, flush=True)
-        if want("c2_ragged"):
-            results["dense_vs_sparse_ragged"] = bench_workload("c2_ragged", w2, dev, args.steps, args.warmup,
+        if want("dense_vs_sparse_paged"):
+            results["dense_vs_sparse_paged_ps1"] = bench_workload("dense_vs_sparse_paged", w2, dev, args.steps, args.warmup)
+            print(f"# dense_vs_sparse paged: {results['dense_vs_sparse_paged_ps1']}", file=sys.stderr, flush=True)
+        if want("dense_vs_sparse_ragged"):
+            results["dense_vs_sparse_ragged"] = bench_workload("dense_vs_sparse_ragged", w2, dev, args.steps, args.warmup,
                                                                ragged=True)
-            print(f"# c2 ragged: {results['dense_vs_sparse_ragged']}", file=sys.stderr, flush=True)
+            print(f"# dense_vs_sparse ragged: {results['dense_vs_sparse_ragged']}", file=sys.stderr, flush=True)
         w2.k = w2.v = None
-    if want("c3"):
+    if want("gqa_append"):
         w3 = W.gqa_append(device=dev)
-        results["gqa_append"] = bench_workload("c3", w3, dev, args.steps, args.warmup)
-        print(f"# c3: {results['gqa_append']}", file=sys.stderr, flush=True)
+        results["gqa_append"] = bench_workload("gqa_append", w3, dev, args.steps, args.warmup)
+        print(f"# gqa_append: {results['gqa_append']}", file=sys.stderr, flush=True)
         del w3
-    if want("c4"):
+    if want("long_causal"):
         w4 = W.long_causal(device=dev)
-        results["long_causal"] = bench_workload("c4", w4, dev, args.steps, args.warmup)
-        print(f"# c4: {results['long_causal']}", file=sys.stderr, flush=True)
+        results["long_causal"] = bench_workload("long_causal", w4, dev, args.steps, args.warmup)
+        print(f"# long_causal: {results['long_causal']}", file=sys.stderr, flush=True)
         del w4
-    if want("c5"):
+    if want("batch_decode"):
         w5 = W.batch_decode(device=dev)
-        results["batch_decode"] = bench_workload("c5", w5, dev, args.steps, args.warmup)
-        print(f"# c5: {results['batch_decode']}", file=sys.stderr, flush=True)
+        results["batch_decode"] = bench_workload("batch_decode", w5, dev, args.steps, args.warmup)
+        print(f"# batch_decode: {results['batch_decode']}", file=sys.stderr, flush=True)
         del w5
     if want("append"):
         wa = W.chunk_append(device=dev)
@@ -449,7 +449,7 @@ def main():
     traffic = load_traffic()
     roofline = {"bound": "mfma", "achieved": main_r["TFLOP_per_s"], "peak": PEAK_BF16_TFLOPS,
                 "unit": "TFLOP/s", "frac": main_r["TFLOP_per_s"] / PEAK_BF16_TFLOPS,
-                "traffic": traffic.get("c2_paged_bytes_per_launch") if traffic else None,
+                "traffic": traffic.get("dense_vs_sparse_paged_bytes_per_launch") if traffic else None,
                 "kernel": "prefill_kernel<128, paged, causal>",
                 "per_launch_flops": main_r["algorithmic_flops"], "avg_launch_ms": main_r["launch_ms_avg"]}
     line = {
