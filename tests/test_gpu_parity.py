@@ -166,6 +166,25 @@ def test_decode_ragged():
     compare(o, lse, *oracle_paged(w), "decode ragged")
 
 
+@pytest.mark.parametrize("Hq,Hkv", [(12, 4), (24, 4), (10, 2), (32, 1)])
+def test_group_sizes_not_powers_of_two(Hq, Hkv):
+    """Packed row = token * G + head in group, so with G = 3, 5 or 6 a wave's
+    32 rows start and end mid-token; G = 32 is past the decode kernel's 16
+    heads per KV head, and its single-token batches take the prefill kernel."""
+    G = Hq // Hkv
+    w = W.build(f"grp{G}", 80 + G, [37, 1, 70, 5, 130], [300, 19, 70, 5, 131], Hq, Hkv, 128, 16,
+                causal=True, pool_slack=0.1)
+    o, lse, info = run_paged(w)
+    assert info["kernel"] == pka.PKA_KERNEL_PREFILL
+    compare(o, lse, *oracle_paged(w), f"prefill G={G}")
+    wd = W.batch_decode(seed=90 + G, batch=10, kv_log2_range=(0.0, 11.0), kv_clamp=(1, 2000), head_dim=128,
+                        heads=Hq, kv_heads=Hkv, page_size=16)
+    for split in (True, False):
+        o, lse, info = run_paged(wd, disable_split_kv=not split)
+        assert info["kernel"] == (pka.PKA_KERNEL_DECODE if G <= 16 else pka.PKA_KERNEL_PREFILL)
+        compare(o, lse, *oracle_paged(wd), f"decode G={G} split={split}")
+
+
 @pytest.mark.parametrize("D", [64, 128])
 def test_prefill_non_causal(D):
     w = W.build("nc", 62 + D, [130, 7, 300], [400, 7, 90], 8, 2, D, 16, causal=False, pool_slack=0.2)
