@@ -27,7 +27,7 @@ def _mixed(seed, D=128, ps=16, ragged=False):
     rng = random.Random(500 + seed)
     B = rng.randint(6, 40)
     Hkv = rng.choice([1, 2, 8])
-    G = rng.choice([1, 4, 8])
+    G = rng.choice([1, 3, 4, 6, 8])
     qo = [rng.choice([1, 1, 1, 0, rng.randint(2, 400)]) for _ in range(B)]
     i, j = rng.sample(range(B), 2)
     qo[i], qo[j] = rng.randint(2, 400), 1
