@@ -62,6 +62,15 @@ def test_decode_layouts(ps):
     _check_layouts(w, f"decode ps={ps}")
 
 
+@pytest.mark.parametrize("decode", [False, True])
+def test_layouts_head_dim_64_group_6(decode):
+    """Head strides at D=64 with six query heads per KV head."""
+    qo = [1] * 9 if decode else [20, 1, 77, 6]
+    kv = [3, 40, 129, 1, 300, 64, 65, 2, 17] if decode else [20, 33, 200, 6]
+    w = W.build(f"layouts_g6_{decode}", 75 + decode, qo, kv, 12, 2, 64, 4, causal=True, pool_slack=0.1)
+    _check_layouts(w, f"D=64 G=6 decode={decode}")
+
+
 def test_strided_rejects_bad_strides():
     w = W.tiny()
     dev = cuda()
