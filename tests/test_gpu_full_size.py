@@ -116,3 +116,21 @@ def test_batch_decode_full():
     print(f"batch_decode: oracle on all {w.total_q} rows in {time.time() - t0:.1f} s", flush=True)
     err = compare(o, lse, ref_o, ref_l, "batch_decode")
     print(f"batch_decode: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
+
+
+def test_very_long_kv():
+    """KV far past the benchmark sizes: decode rows over 131072, 3 and 4096
+    keys (many split chunks per row, so large merge groups), and an
+    append chunk of 200 queries over a 100000-token prefix, on sampled rows."""
+    w = W.build("long_kv_decode", 31, [1, 1, 1], [131072, 3, 4096], 32, 8, 128, 16, causal=True,
+                pool_slack=0.01, device=cuda())
+    o, lse, info = _run_paged(w)
+    assert info["kernel"] == pka.PKA_KERNEL_DECODE and info["num_merge_groups"] > 0
+    ref_o, ref_l = oracle_paged(_to_cpu(w))
+    compare(o, lse, ref_o, ref_l, "long kv decode")
+    del w
+    w = W.build("long_kv_append", 32, [200], [100200], 32, 8, 128, 16, causal=True, pool_slack=0.01,
+                device=cuda())
+    o, lse, info = _run_paged(w)
+    assert info["kernel"] == pka.PKA_KERNEL_PREFILL
+    _check_sampled(w, o, lse, 48, 24, "long kv append")
