@@ -128,3 +128,21 @@ def test_shared_prefix_decode_full_size():
     ref_o, ref_l = oracle_paged(w)
     compare(o.float().cpu(), lse.cpu(), ref_o, ref_l, "shared-prefix cascade")
     compare(fo, fl, ref_o, ref_l, "shared-prefix flat")
+
+
+@pytest.mark.parametrize("qo", ["prefill", "decode"])
+def test_cascade_head_dim_64_group_3(qo):
+    """Two levels at D=64, three query heads per KV head, page_size 3: the
+    shared level's key count and every request's own keys end mid-page."""
+    B = 4
+    qo_lens = [1] * B if qo == "decode" else [9, 1, 40, 17]
+    own = [max(o, n) for o, n in zip([22, 5, 61, 17], qo_lens)]
+    groups = [[list(range(B))], [[r] for r in range(B)]]
+    pool, q, levels, tables, qo_indptr, num_pages, (Hq, Hkv, D, ps) = _build(
+        3, groups, [[100], own], qo_lens, ps=3, Hq=6, Hkv=2, D=64)
+    dev = cuda()
+    c = pka.Cascade(levels, Hq, Hkv, D, ps, causal=True, num_pages=num_pages, device=dev)
+    o, lse = c.run(q.to(dev), pool.to(dev))
+    torch.cuda.synchronize()
+    c.close()
+    compare(o.float().cpu(), lse.cpu(), *_oracle(pool, q, tables, qo_indptr, True, ps), f"cascade D=64 G=3 {qo}")
