@@ -90,3 +90,18 @@ def test_graph_stable_update_rejects_kind_change():
     with pytest.raises(pka.PkaError):
         plan.update(wd.qo_indptr, wd.kv_indptr, wd.kv_indices, wd.kv_last_page_len)
     plan.close()
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_graph_replay_head_dim_64_group_6(decode):
+    """D=64, six query heads per KV head, page_size 4: batches of different
+    sizes replayed through one captured graph."""
+    if decode:
+        kvs = [[3, 500, 77, 1200, 9], [64, 65], [2000, 1, 333]]
+        qos = [[1] * len(k) for k in kvs]
+    else:
+        qos = [[30, 7, 100], [1, 64], [200]]
+        kvs = [[60, 7, 300], [40, 64], [900]]
+    ws = [W.build(f"graph_g6_{decode}_{i}", 97 + i, qo, kv, 12, 2, 64, 4, causal=True, num_pages=1200)
+          for i, (qo, kv) in enumerate(zip(qos, kvs))]
+    _replay_batches(ws)
