@@ -45,8 +45,10 @@ KERNEL_SOURCES = ["prefill.hip", "decode.hip", "merge.hip", "device.h", "args.h"
 
 def kernel_source_hash() -> str:
     h = hashlib.sha256()
-    for f in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, "paged_kv_cache_plan_amd", "csrc", f), "rb") as fh:
+    paths = [os.path.join(ROOT, "paged_kv_cache_plan_amd", "csrc", f) for f in KERNEL_SOURCES]
+    paths.append(os.path.join(ROOT, "paged_kv_cache_plan_amd", "build.py"))  # compile flags
+    for path in paths:
+        with open(path, "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -31,7 +31,10 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 # decode takes its next unit with one lane's atomic whose result is awaited
 # only at the unit's end; the atomic optimizer would read it back at once
 # (a wait for every load in flight)
-KERNEL_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
+KERNEL_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
+                # the ILP-first machine scheduler: measured 1-2% faster on the
+                # short causal units of a ragged prefill batch, equal elsewhere
+                "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
 
 
 def _hipcc() -> str:
