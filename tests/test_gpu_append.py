@@ -8,7 +8,7 @@ import torch
 
 from oracle import append as A
 import paged_kv_cache_plan_amd as pka
-from paged_kv_cache_plan_amd import workloads as W
+from inputs import workloads as W
 from tests.gpu_common import cuda
 
 pytestmark = pytest.mark.gpu

@@ -113,7 +113,7 @@ def test_shared_prefix_decode_full_size():
     prefix plus their own 128..1024-token suffixes, Hq=32, Hkv=8, D=128,
     page_size=16), drawn on the GPU as bench.py draws it: the two-level
     cascade and the flat decode plan both match the oracle on every row."""
-    from paged_kv_cache_plan_amd import workloads as W
+    from inputs import workloads as W
     from tests.gpu_common import oracle_paged, run_paged
     dev = cuda()
     w = W.shared_prefix_decode(device=dev)

@@ -9,7 +9,7 @@ import pytest
 import torch
 
 import paged_kv_cache_plan_amd as pka
-from paged_kv_cache_plan_amd import workloads as W
+from inputs import workloads as W
 from tests.gpu_common import compare, cuda, oracle_paged, sample_rows
 
 pytestmark = pytest.mark.gpu

@@ -6,7 +6,7 @@ import torch
 
 import oracle
 import paged_kv_cache_plan_amd as pka
-from paged_kv_cache_plan_amd import workloads as W
+from inputs import workloads as W
 from tests.gpu_common import compare, cuda, oracle_paged, run_paged, run_ragged
 
 pytestmark = pytest.mark.gpu

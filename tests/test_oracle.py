@@ -17,7 +17,7 @@ import torch
 
 import oracle
 from oracle import attention as A
-from paged_kv_cache_plan_amd import workloads as W
+from inputs import workloads as W
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 LN2 = math.log(2.0)
@@ -342,10 +342,43 @@ def pin_recursive_merge_identity():
             _close(acc[1], full_l, 1e-12)
 
 
+def pin_sampled_rows():
+    """batch_attention(rows=R) returns exactly the rows R of the whole-batch
+    result, in R's order, for paged and ragged sources: R is unsorted, spans
+    several requests, repeats a row, and includes rows that see no key (a
+    qo_len > kv_len request and a kv_len 0 request) next to a qo_len 0
+    request."""
+    #          qo  kv
+    # req 0:    5   9    rows 0..4
+    # req 1:    0   4    (no rows)
+    # req 2:    6   3    rows 5..10; rows 5..7 see no key (qo > kv)
+    # req 3:    4   0    rows 11..14; no key at all
+    # req 4:    3   7    rows 15..17
+    w = W.build("rows", 11, [5, 0, 6, 4, 3], [9, 4, 3, 0, 7], 4, 2, 8, 3, causal=True, pool_slack=0.5,
+                ragged=True)
+    R = [16, 12, 0, 7, 5, 14, 3, 10, 9, 1, 13, 6, 3, 17, 2]
+    for src in ("paged", "ragged"):
+        if src == "paged":
+            run = lambda rows: _oracle_paged(w, rows=rows)
+        else:
+            run = lambda rows: oracle.batch_attention_ragged(w.q, w.k, w.v, w.qo_indptr, w.kv_token_indptr,
+                                                             True, w.sm_scale, rows=rows)
+        full_o, full_l = run(None)
+        o, l = run(R)
+        assert torch.equal(o, full_o[R]) and torch.equal(l, full_l[R]), src
+        assert torch.isneginf(full_l[5:8]).all() and torch.isneginf(full_l[11:15]).all()
+        assert torch.isfinite(full_l[8:11]).all() and torch.isfinite(full_l[15:18]).all()
+    # one row alone, as the sampled full-size checks pick them
+    for r in (0, 9, 17):
+        o, l = _oracle_paged(w, rows=[r])
+        full_o, full_l = _oracle_paged(w)
+        assert torch.equal(o[0], full_o[r]) and torch.equal(l[0], full_l[r])
+
+
 PINS = [pin_golden_page_table, pin_golden_attention, pin_golden_merge, pin_brute_force,
         pin_library_sdpa, pin_causal_closed_forms, pin_zero_keys_mean,
         pin_constant_values_and_single_key, pin_gqa_equals_repeated_mha,
-        pin_page_size_and_permutation_invariance, pin_recursive_merge_identity]
+        pin_page_size_and_permutation_invariance, pin_recursive_merge_identity, pin_sampled_rows]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=[p.__name__ for p in PINS])
@@ -442,6 +475,42 @@ def _attention_state_transposed_v(q_rows, K, V, vis, sm_scale):
     return o.flip(-1), lse
 
 
+def _batch_attention_global_local(q, qo_indptr, kv_source, num_kv_heads, causal, sm_scale=None, rows=None):
+    """batch_attention with one planted slip: a selected row's local index
+    is taken as its global row number (local = sel[pick], not sel[pick] - q0)."""
+    total_q, Hq, D = q.shape
+    G = Hq // num_kv_heads
+    scale = (1.0 / math.sqrt(D)) if (sm_scale is None or sm_scale <= 0) else float(sm_scale)
+    sel = torch.arange(total_q) if rows is None else torch.as_tensor(rows, dtype=torch.long)
+    o_out = torch.zeros((sel.numel(), Hq, D), dtype=torch.float64)
+    lse_out = torch.full((sel.numel(), Hq), float("-inf"), dtype=torch.float64)
+    for r in range(len(qo_indptr) - 1):
+        q0, q1 = int(qo_indptr[r]), int(qo_indptr[r + 1])
+        pick = ((sel >= q0) & (sel < q1)).nonzero().flatten()
+        if pick.numel() == 0:
+            continue
+        local = sel[pick]
+        K, V = kv_source(r)
+        vis = A.visibility(q1 - q0, K.shape[0], causal, local)
+        for h in range(Hq):
+            hk = A.kv_head_of(h, G)
+            o, lse = A.attention_state(q[q0 + local.clamp(max=q1 - q0 - 1), h].to(torch.float64),
+                                       K[:, hk], V[:, hk], vis, scale)
+            o_out[pick, h] = o
+            lse_out[pick, h] = lse
+    return o_out, lse_out
+
+
+def _batch_attention_sorted_rows(q, qo_indptr, kv_source, num_kv_heads, causal, sm_scale=None, rows=None):
+    """batch_attention with the sampled rows returned in sorted order, not in
+    the order asked for (a slip only the sampled-row path can make)."""
+    rows = None if rows is None else sorted(int(r) for r in rows)
+    return _ORIG_BATCH(q, qo_indptr, kv_source, num_kv_heads, causal, sm_scale, rows)
+
+
+_ORIG_BATCH = A.batch_attention
+
+
 _ORIG_STATE = A.attention_state
 
 MISTAKES = {
@@ -454,6 +523,8 @@ MISTAKES = {
     "lse_natural_log": ("attention_state", _attention_state_natural_lse),
     "sm_scale_dropped": ("attention_state", _attention_state_no_scale),
     "value_dim_reversed": ("attention_state", _attention_state_transposed_v),
+    "sampled_rows_global_index": ("batch_attention", _batch_attention_global_local),
+    "sampled_rows_sorted": ("batch_attention", _batch_attention_sorted_rows),
 }
 
 
