@@ -9,12 +9,17 @@ already resident in HBM; the plan is made once beforehand, as a serving
 engine plans a batch once and runs it for every layer.  Host planning time
 is reported separately as plan_ms.
 
-The JSON line's value is the causal paged prefill throughput on the
-dense-vs-vector-sparse workload (B=16, L=1024, Hq=Hkv=32, D=128,
-page_size=1, randomly permuted pages), the comparison the FlashInfer 0.2
-release blog benchmarks.  The same run also reports the ragged dense
-baseline, GQA append-prefill, long-context causal prefill (compute-bound)
-and batch decode (HBM-bound) under "workloads".
+The JSON line's value is the long-context causal paged prefill throughput
+(B=2 requests of L=16384, Hq=32, Hkv=8, D=128, page_size=16, randomly
+permuted pages), the compute-bound case, from the wall time of the timed
+steps.  Its roofline is the bf16 MFMA peak.  Batch decode (B=256 single-token
+queries over log-uniform KV lengths in [128, 32768], same heads, page_size
+16), the HBM-bound case, is reported beside it with its own roofline against
+HBM peak (``roofline_decode``).  The dense-vs-vector-sparse comparison the
+FlashInfer 0.2 release blog benchmarks ("performance benchmark": causal,
+head_dim 128, Gaussian inputs; here B=16, L=1024, Hq=Hkv=32, once ragged and
+once paged with page_size 1), GQA append-prefill and the extra rows
+(append, mixed batch, cascade) are under "workloads".
 
 Throughput uses algorithmic work only: prefill flops = 4 D Hq (visible
 query-key pairs); decode bytes = every valid K/V row once + q + o + lse +
@@ -53,9 +58,25 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def visible_pairs(qo_lens, kv_lens, causal=True) -> int:
+    """Number of (query, key) pairs the attention definition visits: with the
+    bottom-right causal mask, row i of a request sees min(kv, max(0, i + kv -
+    qo + 1)) keys; without it, all kv keys."""
+    total = 0
+    for q, k in zip(qo_lens, kv_lens):
+        if not causal:
+            total += q * k
+            continue
+        blind = max(0, q - k)  # rows with i + k - q + 1 <= 0 see no key
+        n = q - blind          # rows that see at least one key: 1, 2, ... n + (k - q) keys
+        if n:
+            first = blind + k - q + 1
+            total += n * first + n * (n - 1) // 2
+    return total
+
+
 def prefill_flops(w) -> float:
-    import paged_kv_cache_plan_amd as pka
-    return 4.0 * w.head_dim * w.num_qo_heads * pka.visible_pairs(w.qo_lens, w.kv_lens, w.causal)
+    return 4.0 * w.head_dim * w.num_qo_heads * visible_pairs(w.qo_lens, w.kv_lens, w.causal)
 
 
 def decode_bytes(w) -> float:
@@ -82,6 +103,24 @@ def make_plan(w, dev, ragged=False):
     plan_ms = (time.perf_counter() - t0) * 1e3
     torch.cuda.synchronize()
     return plan, plan_ms
+
+
+def plan_cost(w, dev, ragged=False, n=10):
+    """Host time of Plan(...) (the library's plan call plus the binding's
+    workspace allocation from torch's caching allocator): the first plan of
+    the workload, then the median of n more create/destroy cycles, as a
+    serving engine plans a new batch every step."""
+    first = None
+    times = []
+    for i in range(n + 1):
+        plan, ms = make_plan(w, dev, ragged)
+        plan.close()
+        if i == 0:
+            first = ms
+        else:
+            times.append(ms)
+    times.sort()
+    return {"plan_ms": times[len(times) // 2], "plan_ms_first": first}
 
 
 WARM_MS = 300.0  # minimum back-to-back warm-up per workload (the GPU's clocks ramp up under load)
@@ -137,11 +176,12 @@ def bench_workload(name, w, dev, steps, warmup, ragged=False, copies=2):
     total_ms, per = time_launches(launch, steps, warmup)
     info = plan.info
     plan.close()
+    cost = plan_cost(w, dev, ragged)
     per_sorted = sorted(per)
     med = per_sorted[len(per) // 2]
     avg = sum(per) / len(per)
     res = {"ms_per_step": total_ms / steps, "launch_ms_avg": avg, "launch_ms_median": med,
-           "launch_ms_min": per_sorted[0], "plan_ms": plan_ms, "units": info["num_units"],
+           "launch_ms_min": per_sorted[0], **cost, "units": info["num_units"],
            "merge_groups": info["num_merge_groups"], "kv_chunk": info["kv_chunk"],
            "kernel": "decode" if info["kernel"] == 1 else "prefill"}
     if info["kernel"] == 1:
@@ -257,7 +297,7 @@ def bench_mixed(w, dev, steps, warmup, copies=2):
         res[f"{name}_ms_median"] = sorted(per)[len(per) // 2]
     for p in (plan_mixed, plan_whole, plan_p, plan_d):
         p.close()
-    flop = 4.0 * D * H * pka.visible_pairs([w.qo_lens[r] for r in pre], [w.kv_lens[r] for r in pre], w.causal)
+    flop = 4.0 * D * H * visible_pairs([w.qo_lens[r] for r in pre], [w.kv_lens[r] for r in pre], w.causal)
     kv_bytes = 4.0 * w.num_kv_heads * D * sum(w.kv_lens[r] for r in dec)
     t = res["mixed_ms_avg"] * 1e-3
     res.update({"prefill_flops": flop, "decode_kv_bytes": kv_bytes,
@@ -315,31 +355,128 @@ def bench_cascade(w, dev, steps, warmup, copies=2):
     return res
 
 
-def cpu_baseline(w, budget_s=10.0):
-    """The CPU fp64 oracle, as it stands, on a bounded sample of the headline
-    workload (the same inputs the GPU was timed on, copied to the host):
-    whole requests (all heads, all rows), request after request and pass
-    after pass over the batch, until ~budget_s seconds of CPU work."""
+def _host_sub_batch(w, rs, kv_head):
+    """Requests rs of workload w restricted to one KV head and its group of
+    query heads, as host tensors: (q, pool, qo_indptr, kv_indptr, kv_indices,
+    kv_last_page_len, qo_lens, kv_lens).  The pool keeps every page (so the
+    page ids stay valid) but only the one KV head."""
+    import torch
+    G = w.num_qo_heads // w.num_kv_heads
+    qo, kv, idx, last, rows = [0], [0], [], [], []
+    for r in rs:
+        a, b = int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])
+        rows.append((a, b))
+        qo.append(qo[-1] + b - a)
+        pa, pb = int(w.kv_indptr[r]), int(w.kv_indptr[r + 1])
+        kv.append(kv[-1] + pb - pa)
+        idx += w.kv_indices[pa:pb].tolist()
+        last.append(int(w.kv_last_page_len[r]))
+    heads = slice(kv_head * G, (kv_head + 1) * G)
+    q = torch.cat([w.q[a:b, heads] for a, b in rows]).cpu()
+    pool = w.paged_kv[:, :, :, kv_head:kv_head + 1].cpu()
+    i32 = lambda x: torch.tensor(x, dtype=torch.int32)
+    return (q, pool, i32(qo), i32(kv), i32(idx), i32(last), [w.qo_lens[r] for r in rs],
+            [w.kv_lens[r] for r in rs])
+
+
+def cpu_baseline_prefill(sample, head_dim, sm_scale, budget_s=10.0):
+    """The CPU fp64 oracle, as it stands, on a bounded sample of the
+    long-context causal workload: whole requests (every row) for one KV head
+    and its group of query heads, request after request, until at least
+    budget_s seconds of CPU work.  Throughput is the sample's algorithmic
+    flops over its time (the same per-pair count as the GPU figure)."""
     import torch
 
     import oracle
-    import paged_kv_cache_plan_amd as pka
-    threads = torch.get_num_threads()
-    w.q, w.paged_kv = w.q.cpu(), w.paged_kv.cpu()
+    q, pool, qo, kv, idx, last, qo_lens, kv_lens = sample
+    G = q.shape[1]
     done, flops, t_total = 0, 0.0, 0.0
-    while t_total < budget_s:
-        r = done % w.batch
-        q0, q1 = int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])
+    while t_total < budget_s and done < 2 * len(qo_lens):
+        r = done % len(qo_lens)
+        a, b = int(qo[r]), int(qo[r + 1])
+        pa, pb = int(kv[r]), int(kv[r + 1])
         t0 = time.perf_counter()
-        oracle.batch_attention_paged(w.q, w.paged_kv, w.qo_indptr, w.kv_indptr, w.kv_indices,
-                                     w.kv_last_page_len, True, w.sm_scale, rows=list(range(q0, q1)))
+        oracle.batch_attention_paged(q[a:b], pool, torch.tensor([0, b - a], dtype=torch.int32),
+                                     torch.tensor([0, pb - pa], dtype=torch.int32), idx[pa:pb], last[r:r + 1],
+                                     True, sm_scale)
         t_total += time.perf_counter() - t0
-        flops += 4.0 * w.head_dim * w.num_qo_heads * pka.visible_pairs([q1 - q0], [w.kv_lens[r]], True)
+        flops += 4.0 * head_dim * G * visible_pairs([qo_lens[r]], [kv_lens[r]], True)
         done += 1
-    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
-            "sample": f"{done} request runs ({done / w.batch:.1f} passes over the {w.batch} requests, all "
-                      f"{w.num_qo_heads} heads, all rows) of the dense-vs-vector-sparse workload, paged "
-                      f"page_size=1, fp64 torch CPU, {t_total:.1f} s", "os_cpu_count": os.cpu_count()}
+    return {"value": flops / t_total / 1e12, "unit": "TFLOP/s", "cores": torch.get_num_threads(),
+            "kind": "oracle", "os_cpu_count": os.cpu_count(), "nproc": _nproc(),
+            "sample": f"{done} whole request(s) of the long-context causal workload (L={qo_lens[0]}, every "
+                      f"row) for one KV head and its {G} query heads, fp64 torch CPU, {t_total:.1f} s; "
+                      f"throughput = the sample's algorithmic flops / its time"}
+
+
+def cpu_baseline_decode(w_host, budget_s=30.0):
+    """The CPU fp64 oracle on the batch-decode workload: requests in batch
+    order, all heads, until the whole batch is done or budget_s has passed;
+    throughput is the algorithmic bytes of the requests done over their time."""
+    import torch
+
+    import oracle
+    q, pool = w_host["q"], w_host["pool"]
+    qo_indptr, kv_indptr, kv_indices, last = (w_host[k] for k in ("qo_indptr", "kv_indptr", "kv_indices", "last"))
+    kv_lens, Hq, Hkv, D = w_host["kv_lens"], q.shape[1], pool.shape[3], q.shape[2]
+    B = len(kv_lens)
+    done, nbytes, t_total = 0, 0.0, 0.0
+    chunk = 16
+    while done < B and t_total < budget_s:
+        rs = list(range(done, min(B, done + chunk)))
+        a, b = int(qo_indptr[rs[0]]), int(qo_indptr[rs[-1] + 1])
+        t0 = time.perf_counter()
+        oracle.batch_attention_paged(q, pool, qo_indptr, kv_indptr, kv_indices, last, True, None,
+                                     rows=list(range(a, b)))
+        t_total += time.perf_counter() - t0
+        nbytes += sum(kv_lens[r] * 2 * Hkv * D * 2 + Hq * D * 4 + Hq * 4 for r in rs)
+        nbytes += 4 * (int(kv_indptr[rs[-1] + 1]) - int(kv_indptr[rs[0]]))
+        done = rs[-1] + 1
+    return {"value": nbytes / t_total / 1e9, "unit": "GB/s", "cores": torch.get_num_threads(), "kind": "oracle",
+            "os_cpu_count": os.cpu_count(), "nproc": _nproc(),
+            "sample": f"{done} of the {B} batch-decode requests (all heads), fp64 torch CPU, {t_total:.1f} s; "
+                      f"throughput = their algorithmic bytes / their time"}
+
+
+def _nproc():
+    import subprocess
+    try:
+        return int(subprocess.run(["nproc"], capture_output=True, text=True, timeout=10).stdout.strip())
+    except Exception:
+        return None
+
+
+def peak_clock_mhz():
+    """The device's peak shader clock (hipDeviceGetAttribute, ClockRate)."""
+    import ctypes
+    try:
+        hip = ctypes.CDLL("libamdhip64.so")
+        v = ctypes.c_int()
+        if hip.hipDeviceGetAttribute(ctypes.byref(v), 5, 0) == 0:  # hipDeviceAttributeClockRate (kHz)
+            return v.value / 1000.0
+    except OSError:
+        pass
+    return None
+
+
+def clock_under_load(launch, n):
+    """The shader clock rocm-smi reports while n launches run back to back
+    (queued first, so that the GPU is busy while rocm-smi reads it)."""
+    import re
+    import subprocess
+
+    import torch
+    torch.cuda.synchronize()
+    for i in range(n):
+        launch(i)
+    try:
+        out = subprocess.run(["rocm-smi", "--showclocks"], capture_output=True, text=True, timeout=30).stdout
+        m = re.search(r"sclk clock level:\s*\d+:\s*\((\d+)\s*Mhz\)", out)
+        mhz = float(m.group(1)) if m else None
+    except Exception:
+        mhz = None
+    torch.cuda.synchronize()
+    return mhz
 
 
 def load_traffic():
@@ -353,6 +490,23 @@ def load_traffic():
     return t
 
 
+def roofline_entry(res, bound, kernel, traffic_key, traffic, clock_mhz, peak_mhz):
+    """Roofline of a workload's attention kernel: algorithmic work per launch
+    over its average launch time (HIP events on the launch stream)."""
+    if bound == "mfma":
+        achieved, peak, unit, work = res["TFLOP_per_s"], PEAK_BF16_TFLOPS, "TFLOP/s", res["algorithmic_flops"]
+    else:
+        achieved, peak, unit, work = res["GB_per_s"], PEAK_HBM_GBS, "GB/s", res["algorithmic_bytes"]
+    e = {"bound": bound, "achieved": achieved, "peak": peak, "unit": unit, "frac": achieved / peak,
+         "traffic": traffic.get(traffic_key) if traffic else None, "kernel": kernel,
+         "per_launch_work": work, "avg_launch_ms": res["launch_ms_avg"],
+         "clock_mhz_under_load": clock_mhz, "peak_clock_mhz": peak_mhz}
+    if bound == "mfma" and clock_mhz and peak_mhz:
+        # the MFMA peak scales with the shader clock; HBM's does not
+        e["frac_at_measured_clock"] = achieved / (peak * clock_mhz / peak_mhz)
+    return e
+
+
 def main():
     global WARM_MS
     ap = argparse.ArgumentParser()
@@ -362,8 +516,10 @@ def main():
     ap.add_argument("--warm-ms", type=float, default=WARM_MS,
                     help="minimum back-to-back warm-up per workload before timing (ms)")
     ap.add_argument("--only", default=None,
-                    help="run one workload: dense_vs_sparse_paged, dense_vs_sparse_ragged, gqa_append, long_causal, batch_decode, append, mixed, cascade (profiling runs)")
+                    help="run one workload: dense_vs_sparse_paged, dense_vs_sparse_ragged, gqa_append, long_causal, "
+                         "batch_decode, append, mixed, cascade (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-clock", action="store_true", help="skip the rocm-smi clock reading")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
     args = ap.parse_args()
@@ -376,7 +532,7 @@ def main():
     import torch
 
     import paged_kv_cache_plan_amd as pka
-    from paged_kv_cache_plan_amd import workloads as W
+    from inputs import workloads as W
     pka.load_library()
     dev = torch.device("cuda", 0)
     torch.cuda.set_device(dev)
@@ -393,52 +549,74 @@ def main():
     prop = torch.cuda.get_device_properties(dev)
     sel = args.only
     results = {}
+    host = {}
+    clock = None
 
     def want(n):
         return sel is None or sel == n
 
-    w2 = None
-    if want("dense_vs_sparse_paged") or want("dense_vs_sparse_ragged"):
-        w2 = W.dense_vs_sparse(device=dev)
-        if want("dense_vs_sparse_paged"):
-            results["dense_vs_sparse_paged_ps1"] = bench_workload("dense_vs_sparse_paged", w2, dev, args.steps, args.warmup)
-            print(f"# dense_vs_sparse paged: {results['dense_vs_sparse_paged_ps1']}", file=sys.stderr, flush=True)
-        if want("dense_vs_sparse_ragged"):
-            results["dense_vs_sparse_ragged"] = bench_workload("dense_vs_sparse_ragged", w2, dev, args.steps, args.warmup,
-                                                               ragged=True)
-            print(f"# dense_vs_sparse ragged: {results['dense_vs_sparse_ragged']}", file=sys.stderr, flush=True)
-        w2.k = w2.v = None
-    if want("gqa_append"):
-        w3 = W.gqa_append(device=dev)
-        results["gqa_append"] = bench_workload("gqa_append", w3, dev, args.steps, args.warmup)
-        print(f"# gqa_append: {results['gqa_append']}", file=sys.stderr, flush=True)
-        del w3
+    def log(name, r):
+        print(f"# {name}: {r}", file=sys.stderr, flush=True)
+
     if want("long_causal"):
         w4 = W.long_causal(device=dev)
         results["long_causal"] = bench_workload("long_causal", w4, dev, args.steps, args.warmup)
-        print(f"# long_causal: {results['long_causal']}", file=sys.stderr, flush=True)
+        log("long_causal", results["long_causal"])
+        if sel is None and not args.no_clock:
+            plan, _ = make_plan(w4, dev)
+            o = torch.empty((w4.total_q, w4.num_qo_heads, w4.head_dim), dtype=torch.bfloat16, device=dev)
+            lse = torch.empty((w4.total_q, w4.num_qo_heads), dtype=torch.float32, device=dev)
+            clock = clock_under_load(lambda i: plan.run(w4.q, w4.paged_kv, o, lse), 300)
+            plan.close()
+            del o, lse
+        if sel is None and not args.no_cpu_baseline:
+            host["long_causal"] = _host_sub_batch(w4, [0, 1], 0)
         del w4
+        torch.cuda.empty_cache()
     if want("batch_decode"):
         w5 = W.batch_decode(device=dev)
         results["batch_decode"] = bench_workload("batch_decode", w5, dev, args.steps, args.warmup)
-        print(f"# batch_decode: {results['batch_decode']}", file=sys.stderr, flush=True)
+        log("batch_decode", results["batch_decode"])
+        if sel is None and not args.no_cpu_baseline:
+            host["batch_decode"] = {"q": w5.q.cpu(), "pool": w5.paged_kv.cpu(), "qo_indptr": w5.qo_indptr,
+                                    "kv_indptr": w5.kv_indptr, "kv_indices": w5.kv_indices,
+                                    "last": w5.kv_last_page_len, "kv_lens": list(w5.kv_lens)}
         del w5
+        torch.cuda.empty_cache()
+    if want("dense_vs_sparse_paged") or want("dense_vs_sparse_ragged"):
+        w2 = W.dense_vs_sparse(device=dev)
+        if want("dense_vs_sparse_paged"):
+            results["dense_vs_sparse_paged_ps1"] = bench_workload("dense_vs_sparse_paged", w2, dev, args.steps,
+                                                                  args.warmup)
+            log("dense_vs_sparse paged", results["dense_vs_sparse_paged_ps1"])
+        if want("dense_vs_sparse_ragged"):
+            results["dense_vs_sparse_ragged"] = bench_workload("dense_vs_sparse_ragged", w2, dev, args.steps,
+                                                               args.warmup, ragged=True)
+            log("dense_vs_sparse ragged", results["dense_vs_sparse_ragged"])
+        del w2
+        torch.cuda.empty_cache()
+    if want("gqa_append"):
+        w3 = W.gqa_append(device=dev)
+        results["gqa_append"] = bench_workload("gqa_append", w3, dev, args.steps, args.warmup)
+        log("gqa_append", results["gqa_append"])
+        del w3
+        torch.cuda.empty_cache()
     if want("append"):
         wa = W.chunk_append(device=dev)
         results["chunk_append"] = bench_append(wa, dev, args.steps, args.warmup)
-        print(f"# append: {results['chunk_append']}", file=sys.stderr, flush=True)
+        log("append", results["chunk_append"])
         del wa
-    torch.cuda.empty_cache()
+        torch.cuda.empty_cache()
     if want("mixed"):
         wm = W.mixed_batch(device=dev)
         results["mixed_batch"] = bench_mixed(wm, dev, args.steps, args.warmup)
-        print(f"# mixed: {results['mixed_batch']}", file=sys.stderr, flush=True)
+        log("mixed", results["mixed_batch"])
         del wm
         torch.cuda.empty_cache()
     if want("cascade"):
         wc = W.shared_prefix_decode(device=dev)
         results["shared_prefix_decode"] = bench_cascade(wc, dev, args.steps, args.warmup)
-        print(f"# cascade: {results['shared_prefix_decode']}", file=sys.stderr, flush=True)
+        log("cascade", results["shared_prefix_decode"])
         del wc
         torch.cuda.empty_cache()
 
@@ -446,39 +624,52 @@ def main():
         print(json.dumps({"only": sel, "results": results}))
         return
 
-    main_r = results["dense_vs_sparse_paged_ps1"]
-    rag = results["dense_vs_sparse_ragged"]
+    c4 = results["long_causal"]
+    c5 = results["batch_decode"]
+    paged, rag = results["dense_vs_sparse_paged_ps1"], results["dense_vs_sparse_ragged"]
     traffic = load_traffic()
-    roofline = {"bound": "mfma", "achieved": main_r["TFLOP_per_s"], "peak": PEAK_BF16_TFLOPS,
-                "unit": "TFLOP/s", "frac": main_r["TFLOP_per_s"] / PEAK_BF16_TFLOPS,
-                "traffic": traffic.get("dense_vs_sparse_paged_bytes_per_launch") if traffic else None,
-                "kernel": "prefill_kernel<128, paged, causal>",
-                "per_launch_flops": main_r["algorithmic_flops"], "avg_launch_ms": main_r["launch_ms_avg"]}
+    peak_mhz = peak_clock_mhz()
+    value = c4["algorithmic_flops"] / (c4["ms_per_step"] * 1e-3) / 1e12
+    roofline = roofline_entry(c4, "mfma", "prefill_kernel<128, paged (page_size 16), causal>", "long_causal",
+                              traffic, clock, peak_mhz)
+    roofline_decode = roofline_entry(c5, "hbm", "decode_kernel<128, paged (page_size 16)> + split merge",
+                                     "batch_decode", traffic, None, peak_mhz)
+    decode_value = c5["algorithmic_bytes"] / (c5["ms_per_step"] * 1e-3) / 1e9
     line = {
         "metric": METRIC,
-        "value": main_r["TFLOP_per_s"],
+        "value": value,
         "unit": "TFLOP/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": main_r["ms_per_step"],
+        "ms_per_step": c4["ms_per_step"],
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": "bf16",
         "data": "synthetic",
-        "config": {"workload": "dense_vs_vector_sparse causal paged prefill: B=16, L=1024, Hq=Hkv=32, "
-                               "D=128, page_size=1, randomly permuted pages",
-                   "batch": 16, "seq_len": 1024, "num_qo_heads": 32, "num_kv_heads": 32, "head_dim": 128,
-                   "page_size": 1, "parallelism": "single GPU"},
+        "config": {"workload": "long-context causal paged prefill: B=2 requests of L=16384, Hq=32, Hkv=8, "
+                               "D=128, page_size=16, randomly permuted pages",
+                   "batch": 2, "seq_len": 16384, "num_qo_heads": 32, "num_kv_heads": 8, "head_dim": 128,
+                   "page_size": 16, "parallelism": "single GPU"},
         "roofline": roofline,
-        "paged_over_ragged": main_r["TFLOP_per_s"] / rag["TFLOP_per_s"],
-        "device": {"name": prop.name, "compute_units": prop.multi_processor_count,
-                   "clock_khz": getattr(prop, "clock_rate", None)},
+        "decode": {"workload": "batch decode: B=256 single-token queries, KV lengths log-uniform in "
+                               "[128, 32768], Hq=32, Hkv=8, D=128, page_size=16, split-KV + merge",
+                   "value": decode_value, "unit": "GB/s", "ms_per_step": c5["ms_per_step"]},
+        "roofline_decode": roofline_decode,
+        "paged_over_ragged": paged["TFLOP_per_s"] / rag["TFLOP_per_s"],
+        "gates": {"long_causal_ge_50pct_bf16_peak": value / PEAK_BF16_TFLOPS >= 0.50,
+                  "batch_decode_ge_70pct_hbm_peak": decode_value / PEAK_HBM_GBS >= 0.70,
+                  "page_size_1_within_10pct_of_ragged": paged["TFLOP_per_s"] / rag["TFLOP_per_s"] >= 0.90},
+        "device": {"name": prop.name, "compute_units": prop.multi_processor_count, "peak_clock_mhz": peak_mhz,
+                   "clock_mhz_under_load": clock},
         "workloads": results,
     }
     if not args.no_cpu_baseline:
-        line["cpu_baseline"] = cpu_baseline(w2)
+        import torch as _t
+        _t.set_num_threads(min(os.cpu_count() or 1, 16))
+        line["cpu_baseline"] = cpu_baseline_prefill(host.pop("long_causal"), 128, 1.0 / (128 ** 0.5))
+        line["cpu_baseline_decode"] = cpu_baseline_decode(host.pop("batch_decode"))
     print(json.dumps(line))
 
 

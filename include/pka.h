@@ -31,8 +31,13 @@
  * Plan / run split (FlashInfer 0.2 release blog, "faster plan function"): the
  * plan reads its index arrays from HOST memory, copies what the kernels need
  * into a caller-owned device workspace with an asynchronous host-to-device
- * copy on the caller's stream, and never synchronises.  One plan may be run
- * many times (for instance once per layer) on any q / KV of the planned shape.
+ * copy on the caller's stream, and never waits for the device.  The copy
+ * reads pinned staging buffers that the library keeps in a process-wide pool:
+ * once the pool holds buffers of the sizes in use, creating, updating and
+ * destroying plans allocates and frees no pinned memory (the first plans of a
+ * process allocate it, which HIP may serialise with device work).  One plan
+ * may be run many times (for instance once per layer) on any q / KV of the
+ * planned shape.
  *
  * Errors: every int-returning call returns PKA_OK (0) or a PKA_ERR_* code and
  * records a message readable with pka_last_error() (per thread).  No call
@@ -114,9 +119,17 @@ typedef struct pka_plan_info {
 const char* pka_last_error(void);
 
 /*
- * Workspace sizes for a plan of this batch.  Pure host call; reads host
- * arrays qo_indptr[batch+1], kv_indptr[batch+1] and (paged) kv_last_page_len[batch].
- * Writes the byte counts the two device workspaces of pka_plan_create need.
+ * Workspace sizes for a plan of this batch, so that the caller can allocate
+ * them before planning (FlashInfer 0.2 release blog, "CUDAGraph compatibility
+ * for variable-length inputs": the workspaces a plan writes are sized up
+ * front; a graph-stable caller sizes them once for its largest batch).  Pure
+ * host call; reads host arrays qo_indptr[batch+1], kv_indptr[batch+1] and
+ * (paged) kv_last_page_len[batch].  Writes the byte counts the two device
+ * workspaces of pka_plan_create need for exactly this batch.  The work
+ * decomposition it computes is kept (per thread) and reused by the next
+ * pka_plan_create of the same batch on this thread, so that the pair plans
+ * once.  Errors as pka_plan_create (except the page-id checks, which need
+ * kv_indices).
  */
 int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
                             const int32_t* kv_last_page_len, int32_t batch,
@@ -135,8 +148,11 @@ int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
  *   other plan, while this plan is in use.
  *   stream: the plan's host-to-device copy is enqueued on it; a run on another
  *   stream must be ordered after it by the caller.
- *   *out receives a library-owned plan.  The plan owns pinned staging memory
- *   read by the enqueued copy, so it must outlive that copy.
+ *   *out receives a library-owned plan.  The pinned staging its copy reads
+ *   is held by the plan until pka_plan_destroy, so the plan must outlive
+ *   that copy.
+ * PKA_ERR_WORKSPACE when a workspace is smaller than this batch needs; the
+ * sizes are checked before anything is allocated or enqueued.
  * Validation (PKA_ERR_INVALID_ARG): indptr arrays start at 0 and never
  * decrease; kv_indptr[batch] == nnz_pages; for a request with pages,
  * 1 <= kv_last_page_len <= page_size, and 0 when it has none; ids in range.
@@ -193,7 +209,16 @@ int pka_run_paged_strided(const pka_plan* plan, const void* q, const void* k_cac
                           const void* v_cache, int64_t page_stride, int64_t slot_stride,
                           int64_t head_stride, void* o, float* lse, pka_stream_t stream);
 
-/* Attention over ragged dense K/V (plan made with PKA_RAGGED_KV). */
+/*
+ * Attention over ragged dense K/V (plan made with PKA_RAGGED_KV): the dense
+ * variable-length problem that paged attention with page_size = 1 must match
+ * (FlashInfer 0.2 release blog, "performance benchmark": the vector-sparse
+ * kernel is compared with dense variable-length attention on the same
+ * inputs; "flexible block sparsity and vector sparsity": both run one kernel
+ * that differs only in where K/V rows are read).  Request r's keys are rows
+ * kv_indptr[r] .. kv_indptr[r+1]-1 of k and v, bf16 [total_kv, Hkv, D];
+ * q, o, lse and errors as pka_run.
+ */
 int pka_run_ragged(const pka_plan* plan, const void* q, const void* k, const void* v, void* o,
                    float* lse, pka_stream_t stream);
 
@@ -278,18 +303,23 @@ int pka_append_paged_kv(const void* append_k, const void* append_v, const int32_
  * head_dim, page_size, pool, causal flag, sm_scale and flags; host arrays as
  * for pka_plan_create).  The new image is uploaded on `stream`; runs ordered
  * after it on that stream see the new batch, and a graph-stable plan's
- * captured runs replay it.  The call waits for the plan's previous upload
- * (a host copy only, never for kernels).  The workspaces given at creation
- * must be large enough (PKA_ERR_WORKSPACE); a graph-stable plan cannot move
- * between prefill and decode batches (PKA_ERR_INVALID_ARG).
+ * captured runs replay it.  The call never waits for the device: it stages
+ * the image in one of the plan's two pinned buffers whose previous copy has
+ * completed (an event query), or in another buffer from the pool when both
+ * are still being read.  The workspaces given at creation must be large
+ * enough (PKA_ERR_WORKSPACE); a graph-stable plan cannot move between prefill
+ * and decode batches (PKA_ERR_INVALID_ARG).
  */
 int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
                     const int32_t* kv_indices, const int32_t* kv_last_page_len, int32_t batch,
                     int32_t nnz_pages, pka_stream_t stream);
 
-/* Free a plan.  The caller must first make sure the plan's copy and every run
- * using it have completed (for example by synchronising the stream).  NULL is
- * a no-op. */
+/* Free a plan.  The caller must first make sure every run using it has
+ * completed (for example by synchronising the stream).  Its staging buffers
+ * return to the library's pool with the events of their last copies (a
+ * buffer is reused only once its copy has completed), so destroying a plan
+ * frees no pinned memory and does not wait.  A mixed-batch plan also
+ * destroys its side stream.  NULL is a no-op. */
 void pka_plan_destroy(pka_plan* plan);
 
 #ifdef __cplusplus

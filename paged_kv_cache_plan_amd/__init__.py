@@ -66,51 +66,49 @@ class PkaError(RuntimeError):
 _lib = None
 
 
-def load_library(path: str = LIB_PATH):
-    """Load libpka.so and declare its signatures (no GPU needed to load)."""
+def load_library(path: Optional[str] = None):
+    """Load libpka.so and declare its signatures (no GPU needed to load).
+
+    ``path`` (or the PKA_LIBRARY environment variable) selects another build
+    of the library, such as the host-only planner library built under the
+    host sanitizers; signatures of functions a library lacks are skipped, and
+    calling one raises AttributeError."""
     global _lib
     if _lib is not None:
         return _lib
+    path = path or os.environ.get("PKA_LIBRARY") or LIB_PATH
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run `python -m paged_kv_cache_plan_amd.build`")
     L = ctypes.CDLL(path)
     i32p = ctypes.POINTER(ctypes.c_int32)
     vp, i32, u32, szp = ctypes.c_void_p, ctypes.c_int32, ctypes.c_uint32, ctypes.POINTER(ctypes.c_size_t)
-    L.pka_last_error.restype = ctypes.c_char_p
-    L.pka_last_error.argtypes = []
-    L.pka_plan_workspace_size.restype = ctypes.c_int
-    L.pka_plan_workspace_size.argtypes = [i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, u32, szp, szp]
-    L.pka_plan_create.restype = ctypes.c_int
-    L.pka_plan_create.argtypes = [i32p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32, i32,
-                                  ctypes.c_float, u32, vp, ctypes.c_size_t, vp, ctypes.c_size_t, vp,
-                                  ctypes.POINTER(vp)]
-    L.pka_plan_get_info.restype = ctypes.c_int
-    L.pka_plan_get_info.argtypes = [vp, ctypes.POINTER(PlanInfo)]
-    L.pka_plan_host_image.restype = ctypes.c_int
-    L.pka_plan_host_image.argtypes = [i32p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32, i32,
-                                      u32, vp, ctypes.c_size_t, ctypes.POINTER(PlanInfo)]
-    L.pka_run.restype = ctypes.c_int
-    L.pka_run.argtypes = [vp, vp, vp, vp, vp, vp]
-    L.pka_run_ragged.restype = ctypes.c_int
-    L.pka_run_ragged.argtypes = [vp, vp, vp, vp, vp, vp, vp]
-    L.pka_merge_states.restype = ctypes.c_int
-    L.pka_merge_states.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, vp, vp, u32, vp]
-    L.pka_debug_gather.restype = ctypes.c_int
-    L.pka_debug_gather.argtypes = [vp, vp, vp, vp, vp]
-    L.pka_merge_states_strided.restype = ctypes.c_int
-    L.pka_merge_states_strided.argtypes = [vp, vp, ctypes.c_int64, i32, i32, i32, ctypes.c_int64, ctypes.c_int64,
-                                           ctypes.c_int64, ctypes.c_int64, vp, vp, u32, vp]
-    L.pka_run_paged_strided.restype = ctypes.c_int
-    L.pka_run_paged_strided.argtypes = [vp, vp, vp, vp, ctypes.c_int64, ctypes.c_int64, ctypes.c_int64, vp, vp,
-                                        vp]
-    L.pka_get_batch_indices_positions.restype = ctypes.c_int
-    L.pka_get_batch_indices_positions.argtypes = [vp, vp, i32, i32, vp, vp, vp]
-    L.pka_append_paged_kv.restype = ctypes.c_int
-    L.pka_append_paged_kv.argtypes = [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, vp]
-    L.pka_plan_update.restype = ctypes.c_int
-    L.pka_plan_update.argtypes = [vp, i32p, i32p, i32p, i32p, i32, i32, vp]
-    L.pka_plan_destroy.restype = None
-    L.pka_plan_destroy.argtypes = [vp]
+    i64, f32, sz = ctypes.c_int64, ctypes.c_float, ctypes.c_size_t
+    c_int = ctypes.c_int
+    sigs = {
+        "pka_last_error": (ctypes.c_char_p, []),
+        "pka_plan_workspace_size": (c_int, [i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, u32, szp, szp]),
+        "pka_plan_create": (c_int, [i32p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32, i32, f32, u32,
+                                    vp, sz, vp, sz, vp, ctypes.POINTER(vp)]),
+        "pka_plan_get_info": (c_int, [vp, ctypes.POINTER(PlanInfo)]),
+        "pka_plan_host_image": (c_int, [i32p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32, i32, u32, vp,
+                                        sz, ctypes.POINTER(PlanInfo)]),
+        "pka_run": (c_int, [vp, vp, vp, vp, vp, vp]),
+        "pka_run_ragged": (c_int, [vp, vp, vp, vp, vp, vp, vp]),
+        "pka_merge_states": (c_int, [vp, vp, i64, i32, i32, i32, vp, vp, u32, vp]),
+        "pka_debug_gather": (c_int, [vp, vp, vp, vp, vp]),
+        "pka_merge_states_strided": (c_int, [vp, vp, i64, i32, i32, i32, i64, i64, i64, i64, vp, vp, u32, vp]),
+        "pka_run_paged_strided": (c_int, [vp, vp, vp, vp, i64, i64, i64, vp, vp, vp]),
+        "pka_get_batch_indices_positions": (c_int, [vp, vp, i32, i32, vp, vp, vp]),
+        "pka_append_paged_kv": (c_int, [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, vp]),
+        "pka_plan_update": (c_int, [vp, i32p, i32p, i32p, i32p, i32, i32, vp]),
+        "pka_plan_destroy": (None, [vp]),
+    }
+    for name, (res, args) in sigs.items():
+        try:
+            fn = getattr(L, name)
+        except AttributeError:
+            continue
+        fn.restype, fn.argtypes = res, args
     _lib = L
     return L
 
@@ -187,6 +185,47 @@ def plan_host_image(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_h
     return img, info.as_dict()
 
 
+class IoShape:
+    """What a plan fixes about the tensors of a run."""
+
+    def __init__(self, total_q, num_qo_heads, num_kv_heads, head_dim, page_size, num_pages, total_kv, out_fp32):
+        self.total_q, self.num_qo_heads, self.num_kv_heads = total_q, num_qo_heads, num_kv_heads
+        self.head_dim, self.page_size, self.num_pages = head_dim, page_size, num_pages
+        self.total_kv, self.out_fp32 = total_kv, out_fp32
+
+
+def check_io(s, q, o, lse, paged_kv=None, k=None, v=None, k_cache=None, v_cache=None):
+    """Check the tensors of a run against the plan before any pointer reaches
+    the library (the C ABI sees raw pointers and cannot): a wrong shape or
+    dtype would make the kernels read or write out of bounds.  Row counts may
+    exceed the plan's (a graph-stable plan runs on buffers sized for its
+    largest batch); the rows past the planned ones are not touched.  Raises
+    ValueError."""
+    import torch
+    Hq, Hkv, D = s.num_qo_heads, s.num_kv_heads, s.head_dim
+
+    def rows_ok(t, n, tail, dtype):
+        return t.dim() == 1 + len(tail) and t.shape[0] >= n and tuple(t.shape[1:]) == tail and t.dtype == dtype
+
+    if not rows_ok(q, s.total_q, (Hq, D), torch.bfloat16):
+        raise ValueError(f"q must be bf16 [>= {s.total_q}, {Hq}, {D}], got {q.dtype} {tuple(q.shape)}")
+    want_o = torch.float32 if s.out_fp32 else torch.bfloat16
+    if not rows_ok(o, s.total_q, (Hq, D), want_o):
+        raise ValueError(f"o must be {want_o} [>= {s.total_q}, {Hq}, {D}] (the plan's output dtype), "
+                         f"got {o.dtype} {tuple(o.shape)}")
+    if lse is not None and not rows_ok(lse, s.total_q, (Hq,), torch.float32):
+        raise ValueError(f"lse must be float32 [>= {s.total_q}, {Hq}], got {lse.dtype} {tuple(lse.shape)}")
+    if paged_kv is not None:
+        if not rows_ok(paged_kv, s.num_pages, (2, s.page_size, Hkv, D), torch.bfloat16):
+            raise ValueError(f"paged_kv must be bf16 [>= {s.num_pages} pages, 2, {s.page_size}, {Hkv}, {D}] "
+                             f"(the plan's pool), got {paged_kv.dtype} {tuple(paged_kv.shape)}")
+    for name, t in (("k", k), ("v", v)):
+        if t is not None and not rows_ok(t, s.total_kv, (Hkv, D), torch.bfloat16):
+            raise ValueError(f"{name} must be bf16 [>= {s.total_kv}, {Hkv}, {D}], got {t.dtype} {tuple(t.shape)}")
+    for name, t in (("k_cache", k_cache), ("v_cache", v_cache)):
+        if t is not None and t.shape[0] < s.num_pages:
+            raise ValueError(f"{name} holds {t.shape[0]} pages; the plan was made for {s.num_pages}")
+
 class Plan:
     """A planned batch: device workspaces plus the library-owned plan handle.
 
@@ -228,6 +267,7 @@ class Plan:
         nnz = 0 if idx is None else idx.numel()
         if num_pages is None:
             num_pages = (int(idx.max()) + 1) if nnz else 0
+        self.num_pages = 0 if ragged else int(num_pages)
         a, b = ctypes.c_size_t(), ctypes.c_size_t()
         _check(L.pka_plan_workspace_size(qo_p, kv_p, last_p, B, num_qo_heads, num_kv_heads, head_dim,
                                          page_size, int(bool(causal)), flags, ctypes.byref(a),
@@ -271,12 +311,17 @@ class Plan:
             lse = torch.empty(shape[:2], dtype=torch.float32, device=q.device)
         return o, lse
 
+    def _io_shape(self):
+        return IoShape(self.total_q, self.num_qo_heads, self.num_kv_heads, self.head_dim, self.page_size,
+                       self.num_pages, int(self.info["total_kv"]), self.out_fp32)
+
     def run(self, q, paged_kv, o=None, lse=None, stream=None):
         """Attention over the paged KV cache; returns (o, lse)."""
         import torch
         if self.ragged:
             raise ValueError("plan was made for ragged K/V: use run_ragged")
         o, lse = self._outputs(q, o, lse)
+        check_io(self._io_shape(), q, o, lse, paged_kv=paged_kv)
         _check(self._lib.pka_run(self._handle, _dev_ptr(q, "q", torch.bfloat16),
                                  _dev_ptr(paged_kv, "paged_kv", torch.bfloat16),
                                  _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
@@ -286,7 +331,10 @@ class Plan:
     def run_ragged(self, q, k, v, o=None, lse=None, stream=None):
         """Attention over ragged dense K/V; returns (o, lse)."""
         import torch
+        if not self.ragged:
+            raise ValueError("plan was made for a paged KV cache: use run")
         o, lse = self._outputs(q, o, lse)
+        check_io(self._io_shape(), q, o, lse, k=k, v=v)
         _check(self._lib.pka_run_ragged(self._handle, _dev_ptr(q, "q", torch.bfloat16),
                                         _dev_ptr(k, "k", torch.bfloat16), _dev_ptr(v, "v", torch.bfloat16),
                                         _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
@@ -314,6 +362,7 @@ class Plan:
         if k_cache.stride() != v_cache.stride():
             raise ValueError("k_cache and v_cache must have the same strides")
         o, lse = self._outputs(q, o, lse)
+        check_io(self._io_shape(), q, o, lse, k_cache=k_cache, v_cache=v_cache)
         ps_, ss, hs = k_cache.stride(0), k_cache.stride(1), k_cache.stride(2)
         _check(self._lib.pka_run_paged_strided(self._handle, _dev_ptr(q, "q", torch.bfloat16),
                                                ctypes.c_void_p(k_cache.data_ptr()),
@@ -467,17 +516,3 @@ def append_paged_kv(append_k, append_v, batch_indices, positions, paged_kv, kv_i
                                  _dev_ptr(kv_indptr, "kv_indptr", torch.int32), kv_indptr.numel() - 1,
                                  _stream_ptr(stream)))
 
-
-def visible_pairs(qo_lens, kv_lens, causal=True) -> int:
-    """Number of (query, key) pairs the attention definition visits (for flop counts)."""
-    total = 0
-    for q, k in zip(qo_lens, kv_lens):
-        if not causal:
-            total += q * k
-            continue
-        # row i sees min(k, max(0, i + k - q + 1)) keys
-        for_lo = max(0, q - k)  # rows with no key: i + k - q + 1 <= 0
-        n = q - for_lo          # rows that see at least one key
-        first = max(1, for_lo + k - q + 1) if n else 0
-        total += n * first + n * (n - 1) // 2 if n else 0
-    return total

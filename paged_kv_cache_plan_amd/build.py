@@ -2,15 +2,18 @@
 
     python -m paged_kv_cache_plan_amd.build
 
-* the planner (plain C++17, no HIP) is compiled with g++;
-* the C ABI (host code against the HIP runtime) with hipcc;
+* the planner and the HIP-free entry points (plain C++17) with g++;
+* the rest of the C ABI (host code against the HIP runtime) with g++ and
+  the HIP headers;
 * the kernels with ``hipcc --offload-arch=gfx950 -O3`` and packed-fp32
   instruction selection switched off (``-Xclang -target-feature -Xclang
   -packed-fp32-ops``); decode also without the atomic optimizer;
 * everything is linked into ``paged_kv_cache_plan_amd/libpka.so``.
 
-A host-only ``libpka_planner_host.so`` (planner + a tiny C shim, no HIP) is
-also built so that planner tests can run under a host sanitizer.
+A host-only ``libpka_planner_host.so`` (the planner and the HIP-free entry
+points of ``host_api.cpp``, no HIP) is also built with AddressSanitizer and
+UndefinedBehaviorSanitizer, so that the planner tests can run against it
+under the host sanitizers (``tests/test_planner_sanitized.py``).
 """
 from __future__ import annotations
 
@@ -23,6 +26,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpka.so")
+HOST_LIB_PATH = os.path.join(HERE, "libpka_planner_host.so")
 ARCH = "gfx950"
 KERNELS = ["prefill.hip", "decode.hip", "merge.hip", "append.hip"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
@@ -75,9 +79,12 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     inc = ["-I", os.path.join(os.path.dirname(HERE), "include"), "-I", CSRC]
     planner_o = os.path.join(BUILD_DIR, "planner.o")
+    host_api_o = os.path.join(BUILD_DIR, "host_api.o")
     api_o = os.path.join(BUILD_DIR, "api.o")
     cmds = [["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
              os.path.join(CSRC, "planner.cpp"), "-o", planner_o],
+            ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-Wextra", *inc, "-c",
+             os.path.join(CSRC, "host_api.cpp"), "-o", host_api_o],
             ["g++", "-O2", "-std=c++17", "-fPIC", "-Wall", "-D__HIP_PLATFORM_AMD__",
              "-I", os.path.join(_rocm(), "include"), *inc, "-c",
              os.path.join(CSRC, "api.cpp"), "-o", api_o]]
@@ -89,9 +96,23 @@ def build(verbose: bool = False) -> str:
     _run_all(cmds, verbose)
     tmp = LIB_PATH + ".tmp"
     _run_all([[hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp,
-               planner_o, api_o, *kobjs]], verbose)
+               planner_o, host_api_o, api_o, *kobjs]], verbose)
     os.replace(tmp, LIB_PATH)
+    build_host_sanitized(verbose)
     return LIB_PATH
+
+
+def build_host_sanitized(verbose: bool = False) -> str:
+    """libpka_planner_host.so: planner.cpp + host_api.cpp under ASan and
+    UBSan (host code only, g++; no GPU code is built with a sanitizer)."""
+    inc = ["-I", os.path.join(os.path.dirname(HERE), "include"), "-I", CSRC]
+    tmp = HOST_LIB_PATH + ".tmp"
+    san = ["g++", "-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer"]
+    srcs = [os.path.join(CSRC, "planner.cpp"), os.path.join(CSRC, "host_api.cpp")]
+    _run_all([[*san, "-O1", "-g", "-std=c++17", "-fPIC", "-shared", "-Wall", "-Wextra", *inc, *srcs, "-o", tmp]],
+             verbose)
+    os.replace(tmp, HOST_LIB_PATH)
+    return HOST_LIB_PATH
 
 
 if __name__ == "__main__":

@@ -1,10 +1,14 @@
-// C ABI of the paged-KV attention library (declared in include/pka.h).
+// C ABI of the paged-KV attention library (declared in include/pka.h): the
+// plan objects, their uploads and the kernel launches.  The HIP-free entry
+// points (size query, host-only planning, error message) are in host_api.cpp.
 //
 // The plan runs the host planner on host index arrays, stages the resulting
-// int workspace image in pinned host memory owned by the plan, and enqueues
-// one asynchronous host-to-device copy on the caller's stream; it never
-// synchronises (FlashInfer 0.2 release blog, "faster plan function").  Runs
-// only enqueue kernels.  Errors become status codes plus a per-thread message.
+// int workspace image in pinned host memory and enqueues one asynchronous
+// host-to-device copy on the caller's stream; it never waits for the device
+// (FlashInfer 0.2 release blog, "faster plan function").  Pinned staging
+// comes from a library-wide pool, so planning in a loop allocates and frees
+// no pinned memory once the pool holds buffers of the sizes in use.  Runs only
+// enqueue kernels.  Errors become status codes plus a per-thread message.
 #include <hip/hip_runtime_api.h>
 
 #include <algorithm>
@@ -13,29 +17,25 @@
 #include <cstdlib>
 #include <cstring>
 #include <exception>
+#include <mutex>
 #include <string>
+#include <vector>
 
 #include "../../include/pka.h"
 #include "args.h"
+#include "host_api.h"
 #include "launch.h"
 #include "planner.h"
 
+using pka::set_error;
+
 namespace {
-
-thread_local std::string g_last_error;
-
-int set_error(int code, const std::string& msg) {
-  g_last_error = msg;
-  return code;
-}
 
 int hip_error(const char* what, hipError_t e) {
   return set_error(PKA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
 constexpr uint32_t kPlanMagic = 0x4e4c5050u;  // "PPLN"
-constexpr uint32_t kKnownFlags =
-    PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV | PKA_GRAPH_STABLE | PKA_MIXED_BATCH;
 
 int env_int(const char* name) {
   const char* s = std::getenv(name);
@@ -51,6 +51,61 @@ struct PartLaunch {
   size_t float_off;   // its partial states inside the float workspace (bytes)
 };
 
+// A pinned host buffer that a plan stages its image in, and the event
+// recorded after the copy that last read it.  The buffer may be reused once
+// that event has completed.
+struct Staging {
+  void* ptr = nullptr;
+  size_t bytes = 0;
+  hipEvent_t copied = nullptr;
+};
+
+// Library-wide pool of staging buffers no plan holds.  Buffers go back to the
+// pool when a plan is destroyed or outgrows them, and stay allocated until
+// the process ends.
+std::mutex g_pool_mu;
+std::vector<Staging> g_pool;
+
+bool copy_done(const Staging& s) { return hipEventQuery(s.copied) == hipSuccess; }
+
+// A free staging buffer of at least `bytes` whose last copy has completed:
+// the smallest such pooled buffer, else a new one (power-of-two size, at
+// least 64 KiB).  Never waits for the device.
+int acquire_staging(size_t bytes, Staging* out) {
+  {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    size_t best = g_pool.size();
+    for (size_t i = 0; i < g_pool.size(); ++i)
+      if (g_pool[i].bytes >= bytes && (best == g_pool.size() || g_pool[i].bytes < g_pool[best].bytes) &&
+          copy_done(g_pool[i]))
+        best = i;
+    if (best < g_pool.size()) {
+      *out = g_pool[best];
+      g_pool.erase(g_pool.begin() + static_cast<std::ptrdiff_t>(best));
+      return PKA_OK;
+    }
+  }
+  size_t sz = 64 << 10;
+  while (sz < bytes) sz *= 2;
+  Staging s;
+  hipError_t e = hipHostMalloc(&s.ptr, sz, hipHostMallocDefault);
+  if (e != hipSuccess) return hip_error("hipHostMalloc(plan staging)", e);
+  e = hipEventCreateWithFlags(&s.copied, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    (void)hipHostFree(s.ptr);
+    return hip_error("hipEventCreateWithFlags(plan staging)", e);
+  }
+  s.bytes = sz;
+  *out = s;
+  return PKA_OK;
+}
+
+void release_staging(std::vector<Staging>* held) {
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  for (const Staging& s : *held) g_pool.push_back(s);
+  held->clear();
+}
+
 }  // namespace
 
 struct pka_plan {
@@ -64,9 +119,10 @@ struct pka_plan {
   size_t partial_lse_offset;
   int32_t off_units, off_req, off_merge, off_idx, off_sched;
   size_t int_ws_bytes, float_ws_bytes;  // capacities of the caller's workspaces
-  void* staging;        // pinned copy of the image, read by the enqueued copy
-  size_t staging_bytes;
-  hipEvent_t uploaded;  // recorded after the image copy
+  // Staging buffers this plan has uploaded from; one whose copy has
+  // completed is reused, otherwise another comes from the pool, so an
+  // update never waits for the device.
+  std::vector<Staging> staging;
   int32_t num_parts;
   PartLaunch parts[2];
   // PKA_MIXED_BATCH: the decode launch runs on `side`, forked from and joined
@@ -77,112 +133,48 @@ struct pka_plan {
 
 namespace {
 
-pka::PlanInput make_input(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
-                          const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages,
-                          int32_t num_pages, int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim,
-                          int32_t page_size, int32_t causal, uint32_t flags, bool check_indices) {
-  pka::PlanInput in;
-  in.qo_indptr = qo_indptr;
-  in.kv_indptr = kv_indptr;
-  in.kv_indices = kv_indices;
-  in.kv_last_page_len = kv_last_page_len;
-  in.batch = batch;
-  in.nnz_pages = nnz_pages;
-  in.num_pages = num_pages;
-  in.num_qo_heads = num_qo_heads;
-  in.num_kv_heads = num_kv_heads;
-  in.head_dim = head_dim;
-  in.page_size = page_size;
-  in.causal = causal;
-  in.flags = flags;
-  in.check_indices = check_indices;
-  in.kv_chunk_override = env_int("PKA_KV_CHUNK");
-  in.prefill_cus_override = env_int("PKA_PREFILL_CUS");
-  return in;
-}
-
-void fill_info(const pka::PlanResult& res, int32_t batch, int32_t nnz, pka_plan_info* info) {
-  info->kernel = res.kernel;
-  info->num_units = res.num_units;
-  info->num_merge_groups = res.num_merge;
-  info->num_partial_rows = res.num_partial_rows;
-  info->block_rows = res.block_rows;
-  info->kv_chunk = res.kv_chunk;
-  info->batch = batch;
-  info->nnz_pages = nnz;
-  info->total_q = res.total_q;
-  info->total_kv = res.total_kv;
-  info->int_ws_bytes = static_cast<int64_t>(res.image.size() * sizeof(int32_t));
-  info->float_ws_bytes = static_cast<int64_t>(res.float_ws_bytes);
-  info->num_workers = res.num_workers;
-  info->num_queues = res.num_queues;
-}
-
-// The whole plan of a batch (one image, or a mixed batch's two).
-struct Planned {
-  pka::MixedPlan mp;
-  const std::vector<int32_t>& image() const { return mp.mixed ? mp.image : mp.single.image; }
-  size_t float_ws_bytes() const { return mp.mixed ? mp.float_ws_bytes : mp.single.float_ws_bytes; }
-};
-
-int plan_or_error(const pka::PlanInput& in, Planned* res) {
-  if (in.flags & ~kKnownFlags) return set_error(PKA_ERR_INVALID_ARG, "unknown flag bits");
-  std::string err;
-  const int st = pka::build_mixed_plan(in, &res->mp, &err);
-  if (st != pka::kOk) return set_error(st, err);
-  return PKA_OK;
-}
-
-void fill_plan_info(const Planned& pl, int32_t batch, int32_t nnz, pka_plan_info* info) {
-  const pka::MixedPlan& mp = pl.mp;
-  if (!mp.mixed) {
-    fill_info(mp.single, batch, nnz, info);
-    info->prefill_cus = info->decode_cus = 0;
-    return;
-  }
-  fill_info(mp.single, batch, nnz, info);  // totals of the whole batch
-  const pka::PlanResult& a = mp.prefill;
-  const pka::PlanResult& b = mp.decode;
-  info->kernel = PKA_KERNEL_MIXED;
-  info->num_units = a.num_units + b.num_units;
-  info->num_merge_groups = a.num_merge + b.num_merge;
-  info->num_partial_rows = a.num_partial_rows + b.num_partial_rows;
-  info->block_rows = a.block_rows;
-  info->kv_chunk = b.kv_chunk;
-  info->int_ws_bytes = static_cast<int64_t>(mp.image.size() * sizeof(int32_t));
-  info->float_ws_bytes = static_cast<int64_t>(mp.float_ws_bytes);
-  info->num_workers = a.num_workers + b.num_workers;
-  info->num_queues = a.num_queues + b.num_queues;
-  info->prefill_cus = mp.prefill_cus;
-  info->decode_cus = mp.decode_cus;
-}
+using pka::Planned;
 
 bool plan_ok(const pka_plan* p) { return p && p->magic == kPlanMagic; }
 
-// Copy a planned image into the plan's pinned staging and enqueue its upload
-// to the int workspace; the staging is reused once the previous upload has
-// completed (host waits on that copy only, never on kernels).
+// Copy a planned image into pinned staging and enqueue its upload to the
+// int workspace, then record the plan's launch facts.  The staging buffer is
+// one of the plan's whose previous copy has completed (checked with an event
+// query, never waited for), or one taken from the pool.
 int upload(pka_plan* p, const Planned& pl, int32_t batch, int32_t nnz, hipStream_t stream) {
   const std::vector<int32_t>& image = pl.image();
   const size_t need = image.size() * sizeof(int32_t);
-  if (p->staging) {
-    const hipError_t w = hipEventSynchronize(p->uploaded);
-    if (w != hipSuccess) return hip_error("hipEventSynchronize(previous plan upload)", w);
+  size_t idx = p->staging.size();
+  for (size_t i = 0; i < p->staging.size(); ++i)
+    if (p->staging[i].bytes >= need && copy_done(p->staging[i])) {
+      idx = i;
+      break;
+    }
+  if (idx == p->staging.size()) {
+    Staging s;
+    const int st = acquire_staging(need, &s);
+    if (st != PKA_OK) return st;
+    // A plan keeps at most two buffers: the smallest other one goes back to
+    // the pool, with its event, so that nobody reuses it before its copy
+    // has completed.
+    if (p->staging.size() >= 2) {
+      size_t drop = 0;
+      for (size_t i = 1; i < p->staging.size(); ++i)
+        if (p->staging[i].bytes < p->staging[drop].bytes) drop = i;
+      std::vector<Staging> back{p->staging[drop]};
+      p->staging.erase(p->staging.begin() + static_cast<std::ptrdiff_t>(drop));
+      release_staging(&back);
+    }
+    p->staging.push_back(s);
+    idx = p->staging.size() - 1;
   }
-  if (need > p->staging_bytes) {
-    if (p->staging) (void)hipHostFree(p->staging);
-    p->staging = nullptr;
-    p->staging_bytes = 0;
-    const hipError_t a = hipHostMalloc(&p->staging, need, hipHostMallocDefault);
-    if (a != hipSuccess) return hip_error("hipHostMalloc(plan staging)", a);
-    p->staging_bytes = need;
-  }
-  std::memcpy(p->staging, image.data(), need);
-  hipError_t e = hipMemcpyAsync(p->int_ws, p->staging, need, hipMemcpyHostToDevice, stream);
+  Staging& slot = p->staging[idx];
+  std::memcpy(slot.ptr, image.data(), need);
+  hipError_t e = hipMemcpyAsync(p->int_ws, slot.ptr, need, hipMemcpyHostToDevice, stream);
   if (e != hipSuccess) return hip_error("hipMemcpyAsync(plan upload)", e);
-  e = hipEventRecord(p->uploaded, stream);
+  e = hipEventRecord(slot.copied, stream);
   if (e != hipSuccess) return hip_error("hipEventRecord(plan upload)", e);
-  fill_plan_info(pl, batch, nnz, &p->info);
+  pka::fill_plan_info(pl, batch, nnz, &p->info);
   const pka::PlanResult& res = pl.mp.single;
   p->partial_lse_offset = res.partial_lse_offset;
   p->off_units = res.image[pka::kHdrOffUnits];
@@ -307,53 +299,6 @@ int run_common(const pka_plan* p, const void* q, const void* k, const void* v, c
 
 extern "C" {
 
-const char* pka_last_error(void) { return g_last_error.c_str(); }
-
-int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
-                            const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
-                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
-                            uint32_t flags, size_t* int_ws_bytes, size_t* float_ws_bytes) {
-  try {
-    if (!int_ws_bytes || !float_ws_bytes) return set_error(PKA_ERR_INVALID_ARG, "null size pointer");
-    if (!kv_indptr || batch < 0) return set_error(PKA_ERR_INVALID_ARG, "kv_indptr must not be NULL");
-    const int32_t nnz = kv_indptr[batch];
-    pka::PlanInput in = make_input(qo_indptr, kv_indptr, nullptr, kv_last_page_len, batch, nnz, 0,
-                                   num_qo_heads, num_kv_heads, head_dim, page_size, causal, flags, false);
-    Planned res;
-    const int st = plan_or_error(in, &res);
-    if (st != PKA_OK) return st;
-    *int_ws_bytes = res.image().size() * sizeof(int32_t);
-    *float_ws_bytes = res.float_ws_bytes();
-    return PKA_OK;
-  } catch (const std::exception& ex) {
-    return set_error(PKA_ERR_INVALID_ARG, ex.what());
-  }
-}
-
-int pka_plan_host_image(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
-                        const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages,
-                        int32_t num_pages_in_pool, int32_t num_qo_heads, int32_t num_kv_heads,
-                        int32_t head_dim, int32_t page_size, int32_t causal, uint32_t flags, void* image,
-                        size_t image_bytes, pka_plan_info* info) {
-  try {
-    pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
-                                   num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
-                                   causal, flags, true);
-    Planned res;
-    const int st = plan_or_error(in, &res);
-    if (st != PKA_OK) return st;
-    if (info) fill_plan_info(res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, info);
-    const size_t need = res.image().size() * sizeof(int32_t);
-    if (image) {
-      if (image_bytes < need) return set_error(PKA_ERR_WORKSPACE, "image buffer too small");
-      std::memcpy(image, res.image().data(), need);
-    }
-    return PKA_OK;
-  } catch (const std::exception& ex) {
-    return set_error(PKA_ERR_INVALID_ARG, ex.what());
-  }
-}
-
 int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
                     const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages, int32_t num_pages_in_pool,
                     int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
@@ -364,11 +309,11 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     *out = nullptr;
     if (!int_ws || !float_ws) return set_error(PKA_ERR_INVALID_ARG, "workspaces must not be NULL");
     if (!std::isfinite(sm_scale)) return set_error(PKA_ERR_INVALID_ARG, "sm_scale must be finite");
-    pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
-                                   num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
-                                   causal, flags, true);
+    pka::PlanInput in = pka::make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
+                                        num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                        causal, flags, true);
     Planned res;
-    int st = plan_or_error(in, &res);
+    int st = pka::plan_for_create(in, &res);
     if (st != PKA_OK) return st;
     const size_t need = res.image().size() * sizeof(int32_t);
     if (int_ws_bytes < need)
@@ -392,15 +337,9 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     p->float_ws = float_ws;
     p->int_ws_bytes = int_ws_bytes;
     p->float_ws_bytes = float_ws_bytes;
-    p->staging = nullptr;
-    p->staging_bytes = 0;
     p->side = nullptr;
     p->fork = p->join = nullptr;
-    hipError_t e = hipEventCreateWithFlags(&p->uploaded, hipEventDisableTiming);
-    if (e != hipSuccess) {
-      delete p;
-      return hip_error("hipEventCreateWithFlags(plan upload)", e);
-    }
+    hipError_t e = hipSuccess;
     if (flags & PKA_MIXED_BATCH) {
       // default priority, like every stream here
       e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
@@ -602,11 +541,11 @@ int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_
                     const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages, pka_stream_t stream) {
   try {
     if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
-    pka::PlanInput in = make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
-                                   plan->num_pages, plan->num_qo_heads, plan->num_kv_heads, plan->head_dim,
-                                   plan->page_size, plan->causal, plan->flags, true);
+    pka::PlanInput in = pka::make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
+                                        plan->num_pages, plan->num_qo_heads, plan->num_kv_heads, plan->head_dim,
+                                        plan->page_size, plan->causal, plan->flags, true);
     Planned res;
-    const int st = plan_or_error(in, &res);
+    const int st = pka::plan_or_error(in, &res);
     if (st != PKA_OK) return st;
     const size_t need = res.image().size() * sizeof(int32_t);
     if (plan->int_ws_bytes < need)
@@ -628,11 +567,10 @@ int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_
 
 void pka_plan_destroy(pka_plan* plan) {
   if (!plan_ok(plan)) return;
-  (void)hipEventDestroy(plan->uploaded);
   if (plan->fork) (void)hipEventDestroy(plan->fork);
   if (plan->join) (void)hipEventDestroy(plan->join);
   if (plan->side) (void)hipStreamDestroy(plan->side);
-  if (plan->staging) (void)hipHostFree(plan->staging);
+  release_staging(&plan->staging);  // pooled with their events, never freed here
   plan->magic = 0;
   delete plan;
 }

@@ -1,0 +1,215 @@
+// The HIP-free entry points of the C ABI (include/pka.h): the size query,
+// host-only planning and the error message.  The plan never needs a GPU to be
+// computed (FlashInfer 0.2 release blog, "faster plan function": planning
+// runs on host arrays), so this file links without the HIP runtime.
+#include "host_api.h"
+
+#include <cstdlib>
+#include <cstring>
+#include <exception>
+
+namespace pka {
+namespace {
+
+thread_local std::string g_last_error;
+
+int env_int(const char* name) {
+  const char* s = std::getenv(name);
+  return s ? std::atoi(s) : 0;
+}
+
+void fill_info(const PlanResult& res, int32_t batch, int32_t nnz, pka_plan_info* info) {
+  info->kernel = res.kernel;
+  info->num_units = res.num_units;
+  info->num_merge_groups = res.num_merge;
+  info->num_partial_rows = res.num_partial_rows;
+  info->block_rows = res.block_rows;
+  info->kv_chunk = res.kv_chunk;
+  info->batch = batch;
+  info->nnz_pages = nnz;
+  info->total_q = res.total_q;
+  info->total_kv = res.total_kv;
+  info->int_ws_bytes = static_cast<int64_t>(res.image.size() * sizeof(int32_t));
+  info->float_ws_bytes = static_cast<int64_t>(res.float_ws_bytes);
+  info->num_workers = res.num_workers;
+  info->num_queues = res.num_queues;
+}
+
+// What a plan's work decomposition depends on: every input but the page ids
+// (which are only validated and copied) and the pool size (only validation).
+struct PlanKey {
+  std::vector<int32_t> qo_indptr, kv_indptr, last;
+  int32_t scalars[9] = {};
+
+  static PlanKey of(const PlanInput& in) {
+    PlanKey k;
+    const int B = in.batch;
+    k.qo_indptr.assign(in.qo_indptr, in.qo_indptr + B + 1);
+    k.kv_indptr.assign(in.kv_indptr, in.kv_indptr + B + 1);
+    if (in.kv_last_page_len && !(in.flags & kFlagRagged)) k.last.assign(in.kv_last_page_len, in.kv_last_page_len + B);
+    const int32_t s[9] = {in.batch, in.num_qo_heads, in.num_kv_heads, in.head_dim, in.page_size, in.causal,
+                          static_cast<int32_t>(in.flags), in.kv_chunk_override, in.prefill_cus_override};
+    std::memcpy(k.scalars, s, sizeof(s));
+    return k;
+  }
+  bool same(const PlanInput& in) const {
+    const int B = in.batch;
+    if (B < 0 || static_cast<size_t>(B) + 1 != qo_indptr.size() || !in.qo_indptr || !in.kv_indptr) return false;
+    const int32_t s[9] = {in.batch, in.num_qo_heads, in.num_kv_heads, in.head_dim, in.page_size, in.causal,
+                          static_cast<int32_t>(in.flags), in.kv_chunk_override, in.prefill_cus_override};
+    if (std::memcmp(s, scalars, sizeof(s)) != 0) return false;
+    if (std::memcmp(in.qo_indptr, qo_indptr.data(), qo_indptr.size() * sizeof(int32_t)) != 0) return false;
+    if (std::memcmp(in.kv_indptr, kv_indptr.data(), kv_indptr.size() * sizeof(int32_t)) != 0) return false;
+    if (!(in.flags & kFlagRagged)) {
+      if (!in.kv_last_page_len || last.size() != static_cast<size_t>(B)) return false;
+      if (std::memcmp(in.kv_last_page_len, last.data(), last.size() * sizeof(int32_t)) != 0) return false;
+    }
+    return true;
+  }
+};
+
+// The last size query's plan on this thread (not for mixed batches, whose
+// sub-batch images carry their own copies of the page ids).
+thread_local bool g_cached = false;
+thread_local PlanKey g_cache_key;
+thread_local Planned g_cache_plan;
+
+}  // namespace
+
+int set_error(int code, const std::string& msg) {
+  g_last_error = msg;
+  return code;
+}
+
+PlanInput make_input(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                     const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages, int32_t num_pages,
+                     int32_t num_qo_heads, int32_t num_kv_heads, int32_t head_dim, int32_t page_size,
+                     int32_t causal, uint32_t flags, bool check_indices) {
+  PlanInput in;
+  in.qo_indptr = qo_indptr;
+  in.kv_indptr = kv_indptr;
+  in.kv_indices = kv_indices;
+  in.kv_last_page_len = kv_last_page_len;
+  in.batch = batch;
+  in.nnz_pages = nnz_pages;
+  in.num_pages = num_pages;
+  in.num_qo_heads = num_qo_heads;
+  in.num_kv_heads = num_kv_heads;
+  in.head_dim = head_dim;
+  in.page_size = page_size;
+  in.causal = causal;
+  in.flags = flags;
+  in.check_indices = check_indices;
+  in.kv_chunk_override = env_int("PKA_KV_CHUNK");
+  in.prefill_cus_override = env_int("PKA_PREFILL_CUS");
+  return in;
+}
+
+int plan_or_error(const PlanInput& in, Planned* res) {
+  if (in.flags & ~kKnownFlags) return set_error(PKA_ERR_INVALID_ARG, "unknown flag bits");
+  std::string err;
+  const int st = build_mixed_plan(in, &res->mp, &err);
+  if (st != kOk) return set_error(st, err);
+  return PKA_OK;
+}
+
+int plan_for_create(const PlanInput& in, Planned* res) {
+  if (g_cached && !(in.flags & kFlagMixed) && g_cache_key.same(in)) {
+    g_cached = false;
+    Planned pl = std::move(g_cache_plan);
+    if (!(in.flags & kFlagRagged)) {
+      if (in.nnz_pages != in.kv_indptr[in.batch])
+        return set_error(PKA_ERR_INVALID_ARG, "kv_indptr[batch] = " + std::to_string(in.kv_indptr[in.batch]) +
+                                                  " but nnz_pages = " + std::to_string(in.nnz_pages));
+      std::string err;
+      const int st = check_page_ids(in.kv_indices, in.nnz_pages, in.num_pages, &err);
+      if (st != kOk) return set_error(st, err);
+      std::vector<int32_t>& im = pl.mp.single.image;
+      if (in.nnz_pages > 0)
+        std::memcpy(im.data() + im[kHdrOffIndices], in.kv_indices, static_cast<size_t>(in.nnz_pages) * sizeof(int32_t));
+    }
+    *res = std::move(pl);
+    return PKA_OK;
+  }
+  return plan_or_error(in, res);
+}
+
+void fill_plan_info(const Planned& pl, int32_t batch, int32_t nnz, pka_plan_info* info) {
+  const MixedPlan& mp = pl.mp;
+  fill_info(mp.single, batch, nnz, info);  // totals of the whole batch
+  info->prefill_cus = info->decode_cus = 0;
+  if (!mp.mixed) return;
+  const PlanResult& a = mp.prefill;
+  const PlanResult& b = mp.decode;
+  info->kernel = PKA_KERNEL_MIXED;
+  info->num_units = a.num_units + b.num_units;
+  info->num_merge_groups = a.num_merge + b.num_merge;
+  info->num_partial_rows = a.num_partial_rows + b.num_partial_rows;
+  info->block_rows = a.block_rows;
+  info->kv_chunk = b.kv_chunk;
+  info->int_ws_bytes = static_cast<int64_t>(mp.image.size() * sizeof(int32_t));
+  info->float_ws_bytes = static_cast<int64_t>(mp.float_ws_bytes);
+  info->num_workers = a.num_workers + b.num_workers;
+  info->num_queues = a.num_queues + b.num_queues;
+  info->prefill_cus = mp.prefill_cus;
+  info->decode_cus = mp.decode_cus;
+}
+
+}  // namespace pka
+
+extern "C" {
+
+const char* pka_last_error(void) { return pka::g_last_error.c_str(); }
+
+int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
+                            const int32_t* kv_last_page_len, int32_t batch, int32_t num_qo_heads,
+                            int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
+                            uint32_t flags, size_t* int_ws_bytes, size_t* float_ws_bytes) {
+  try {
+    if (!int_ws_bytes || !float_ws_bytes) return pka::set_error(PKA_ERR_INVALID_ARG, "null size pointer");
+    if (!kv_indptr || batch < 0) return pka::set_error(PKA_ERR_INVALID_ARG, "kv_indptr must not be NULL");
+    const int32_t nnz = kv_indptr[batch];
+    pka::PlanInput in = pka::make_input(qo_indptr, kv_indptr, nullptr, kv_last_page_len, batch, nnz, 0,
+                                        num_qo_heads, num_kv_heads, head_dim, page_size, causal, flags, false);
+    pka::g_cached = false;
+    pka::Planned res;
+    const int st = pka::plan_or_error(in, &res);
+    if (st != PKA_OK) return st;
+    *int_ws_bytes = res.image().size() * sizeof(int32_t);
+    *float_ws_bytes = res.float_ws_bytes();
+    if (!(flags & PKA_MIXED_BATCH)) {
+      pka::g_cache_key = pka::PlanKey::of(in);
+      pka::g_cache_plan = std::move(res);
+      pka::g_cached = true;
+    }
+    return PKA_OK;
+  } catch (const std::exception& ex) {
+    return pka::set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
+
+int pka_plan_host_image(const int32_t* qo_indptr, const int32_t* kv_indptr, const int32_t* kv_indices,
+                        const int32_t* kv_last_page_len, int32_t batch, int32_t nnz_pages,
+                        int32_t num_pages_in_pool, int32_t num_qo_heads, int32_t num_kv_heads,
+                        int32_t head_dim, int32_t page_size, int32_t causal, uint32_t flags, void* image,
+                        size_t image_bytes, pka_plan_info* info) {
+  try {
+    pka::PlanInput in = pka::make_input(qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
+                                        num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
+                                        causal, flags, true);
+    pka::Planned res;
+    const int st = pka::plan_or_error(in, &res);
+    if (st != PKA_OK) return st;
+    if (info) pka::fill_plan_info(res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, info);
+    const size_t need = res.image().size() * sizeof(int32_t);
+    if (image) {
+      if (image_bytes < need) return pka::set_error(PKA_ERR_WORKSPACE, "image buffer too small");
+      std::memcpy(image, res.image().data(), need);
+    }
+    return PKA_OK;
+  } catch (const std::exception& ex) {
+    return pka::set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
+
+}  // extern "C"

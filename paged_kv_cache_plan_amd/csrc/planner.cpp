@@ -28,6 +28,18 @@ struct Unit {
 
 }  // namespace
 
+int check_page_ids(const int32_t* kv_indices, int32_t nnz, int32_t num_pages, std::string* err) {
+  if (nnz > 0 && !kv_indices) return fail(err, kInvalid, "kv_indices must not be NULL");
+  if (num_pages <= 0 && nnz > 0)
+    return fail(err, kInvalid, "num_pages_in_pool must be positive (got %lld)", num_pages);
+  for (int32_t i = 0; i < nnz; ++i) {
+    const int32_t p = kv_indices[i];
+    if (p < 0 || p >= num_pages)
+      return fail(err, kInvalid, "kv_indices[%lld] = %lld is outside [0, %lld)", i, p, num_pages);
+  }
+  return kOk;
+}
+
 int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   const bool ragged = (in.flags & kFlagRagged) != 0;
   const int B = in.batch;
@@ -64,14 +76,8 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
     if (in.nnz_pages != nnz)
       return fail(err, kInvalid, "kv_indptr[batch] = %lld but nnz_pages = %lld", nnz, in.nnz_pages);
     if (in.check_indices) {
-      if (nnz > 0 && !in.kv_indices) return fail(err, kInvalid, "kv_indices must not be NULL");
-      if (in.num_pages <= 0 && nnz > 0)
-        return fail(err, kInvalid, "num_pages_in_pool must be positive (got %lld)", in.num_pages);
-      for (int32_t i = 0; i < nnz; ++i) {
-        const int32_t p = in.kv_indices[i];
-        if (p < 0 || p >= in.num_pages)
-          return fail(err, kInvalid, "kv_indices[%lld] = %lld is outside [0, %lld)", i, p, in.num_pages);
-      }
+      const int st = check_page_ids(in.kv_indices, nnz, in.num_pages, err);
+      if (st != kOk) return st;
     }
   }
 

@@ -192,6 +192,11 @@ struct PlanResult {
 // Validate and plan.  Returns a Status and fills *err on failure.
 int build_plan(const PlanInput& in, PlanResult* out, std::string* err);
 
+// Every page id of kv_indices[0, nnz) lies in [0, num_pages) (kv_indices may
+// be null only when nnz == 0).  The only use build_plan makes of kv_indices
+// and num_pages besides copying the ids into the image's index section.
+int check_page_ids(const int32_t* kv_indices, int32_t nnz, int32_t num_pages, std::string* err);
+
 // A mixed batch (kFlagMixed with both prefill requests, qo_len > 1, and
 // decode requests, qo_len == 1) runs as two persistent launches side by
 // side: the prefill kernel on part of the compute units and the decode

@@ -16,8 +16,9 @@ import re
 import pytest
 import torch
 
+import bench
 import paged_kv_cache_plan_amd as pka
-from paged_kv_cache_plan_amd import workloads as W
+from inputs import workloads as W
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -218,7 +219,7 @@ def restate_mixed(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, f
         span = kv_indptr[r + 1] - kv_indptr[r]
         return span if ragged else (0 if span == 0 else (span - 1) * ps + last[r])
 
-    flop = sum(4.0 * D * Hq * pka.visible_pairs([qo_len[r]], [kv_len(r)], causal) for r in pre)
+    flop = sum(4.0 * D * Hq * bench.visible_pairs([qo_len[r]], [kv_len(r)], causal) for r in pre)
     nbytes = sum(4.0 * Hkv * D * kv_len(r) for r in dec)
     pcus = restate_mixed_cus(flop, nbytes)
 
@@ -427,7 +428,7 @@ def test_visible_pairs_brute():
         q, k = rng.randint(0, 30), rng.randint(0, 30)
         for causal in (True, False):
             brute = sum(1 for i in range(q) for j in range(k) if not causal or j <= i + k - q)
-            assert pka.visible_pairs([q], [k], causal) == brute
+            assert bench.visible_pairs([q], [k], causal) == brute
 
 
 # ---------------------------------------------------------------------------
@@ -479,7 +480,13 @@ def test_errors():
     rc = L.pka_plan_host_image(i32([0, 3, 5]), i32([0, 2, 3]), None, i32([2, 1]), 2, 3, 8, 4, 2, 64, 4, 1, 0,
                                None, 0, ctypes.byref(info))
     assert rc == E_ARG
-    # run / merge_states / debug_gather reject a bad plan or sizes without a GPU
+
+
+def test_run_errors_without_a_gpu():
+    """run / merge_states / debug_gather reject a bad plan or sizes, and
+    pka_plan_create a too-small workspace, before any HIP call."""
+    L = pka.load_library()
+    E_ARG = pka.PKA_ERR_INVALID_ARG
     assert L.pka_run(None, None, None, None, None, None) == E_ARG
     assert L.pka_run_ragged(None, None, None, None, None, None, None) == E_ARG
     assert L.pka_debug_gather(None, None, None, None, None) == E_ARG
@@ -487,6 +494,33 @@ def test_errors():
     assert L.pka_merge_states(None, None, 4, 2, 1, 66, None, None, 0, None) == E_ARG
     assert L.pka_merge_states(None, None, 0, 2, 1, 64, None, None, 0, None) == pka.PKA_OK  # nothing to do
     L.pka_plan_destroy(None)  # no-op
+    # PKA_ERR_WORKSPACE: the sizes are checked before anything is allocated,
+    # uploaded or dereferenced (the workspace pointers below are never used)
+    i32 = lambda xs: (ctypes.c_int32 * len(xs))(*xs)
+    qo, kv, idx, last = [0, 3, 5], [0, 2, 3], [4, 1, 0], [2, 1]
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    assert L.pka_plan_workspace_size(i32(qo), i32(kv), i32(last), 2, 4, 2, 64, 4, 1, 0, ctypes.byref(a),
+                                     ctypes.byref(b)) == pka.PKA_OK
+    assert a.value > 0 and b.value > 0
+    fake = ctypes.c_void_p(4096)
+    for iw, fw in ((a.value - 4, b.value), (a.value, b.value - 4), (0, 0)):
+        h = ctypes.c_void_p()
+        rc = L.pka_plan_create(i32(qo), i32(kv), i32(idx), i32(last), 2, 3, 8, 4, 2, 64, 4, 1, 0.0, 0, fake, iw,
+                               fake, fw, None, ctypes.byref(h))
+        assert rc == pka.PKA_ERR_WORKSPACE, (iw, fw, L.pka_last_error())
+        assert b"workspace" in L.pka_last_error() and not h.value
+    # after a size query, create still validates the page ids itself
+    assert L.pka_plan_workspace_size(i32(qo), i32(kv), i32(last), 2, 4, 2, 64, 4, 1, 0, ctypes.byref(a),
+                                     ctypes.byref(b)) == pka.PKA_OK
+    h = ctypes.c_void_p()
+    rc = L.pka_plan_create(i32(qo), i32(kv), i32([4, 1, 9]), i32(last), 2, 3, 8, 4, 2, 64, 4, 1, 0.0, 0, fake,
+                           a.value, fake, b.value, None, ctypes.byref(h))
+    assert rc == E_ARG and b"outside" in L.pka_last_error()
+    assert L.pka_plan_workspace_size(i32(qo), i32(kv), i32(last), 2, 4, 2, 64, 4, 1, 0, ctypes.byref(a),
+                                     ctypes.byref(b)) == pka.PKA_OK
+    rc = L.pka_plan_create(i32(qo), i32(kv), i32(idx), i32(last), 2, 2, 8, 4, 2, 64, 4, 1, 0.0, 0, fake,
+                           a.value, fake, b.value, None, ctypes.byref(h))
+    assert rc == E_ARG and b"nnz" in L.pka_last_error()
 
 
 def test_empty_batch_and_edge_lengths():
