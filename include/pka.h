@@ -191,6 +191,22 @@ int pka_run(const pka_plan* plan, const void* q, const void* paged_kv, void* o, 
             pka_stream_t stream);
 
 /*
+ * pka_run for callers that cannot allocate device memory (code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc): the
+ * same kernels and results, but the split-KV partial states go to a static
+ * device scratch array of the library (64 MiB per GPU, held from the first
+ * load of the library on that GPU until the process ends) instead of the
+ * plan's float workspace, which this call never touches.  The call itself
+ * allocates nothing.  Arguments, layouts and ownership as pka_run.
+ * PKA_ERR_WORKSPACE when the plan's partial states (pka_plan_info
+ * float_ws_bytes) exceed 64 MiB.  Every call on one GPU shares that GPU's
+ * scratch: calls that overlap on one GPU (on different streams, or from
+ * several threads without ordering) race and give wrong results.
+ */
+int pka_run_noalloc(const pka_plan* plan, const void* q, const void* paged_kv, void* o, float* lse,
+                    pka_stream_t stream);
+
+/*
  * Attention over a paged KV cache stored with arbitrary strides (plan made
  * without PKA_RAGGED_KV): the HND page layout [num_pages, 2, Hkv, ps, D],
  * separate K and V pools, or pages spaced apart in a larger buffer

@@ -40,7 +40,7 @@ EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka
             "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
             "pka_debug_gather", "pka_plan_destroy", "pka_get_batch_indices_positions",
             "pka_append_paged_kv", "pka_run_paged_strided", "pka_merge_states_strided",
-            "pka_plan_update"]
+            "pka_plan_update", "pka_run_noalloc"]
 
 
 class PlanInfo(ctypes.Structure):
@@ -93,6 +93,7 @@ def load_library(path: Optional[str] = None):
         "pka_plan_host_image": (c_int, [i32p, i32p, i32p, i32p, i32, i32, i32, i32, i32, i32, i32, i32, u32, vp,
                                         sz, ctypes.POINTER(PlanInfo)]),
         "pka_run": (c_int, [vp, vp, vp, vp, vp, vp]),
+        "pka_run_noalloc": (c_int, [vp, vp, vp, vp, vp, vp]),
         "pka_run_ragged": (c_int, [vp, vp, vp, vp, vp, vp, vp]),
         "pka_merge_states": (c_int, [vp, vp, i64, i32, i32, i32, vp, vp, u32, vp]),
         "pka_debug_gather": (c_int, [vp, vp, vp, vp, vp]),
@@ -326,6 +327,22 @@ class Plan:
                                  _dev_ptr(paged_kv, "paged_kv", torch.bfloat16),
                                  _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
                                  _stream_ptr(stream)))
+        return o, lse
+
+    def run_noalloc(self, q, paged_kv, o, lse=None, stream=None):
+        """pka_run_noalloc: as run, with the split-KV partial states in the
+        library's static device scratch; o (and lse) must be given, so that
+        the call allocates nothing.  Calls that overlap on one GPU race."""
+        import torch
+        if self.ragged:
+            raise ValueError("plan was made for ragged K/V: use run_ragged")
+        if o is None:
+            raise ValueError("run_noalloc allocates nothing: pass o (and lse)")
+        check_io(self._io_shape(), q, o, lse, paged_kv=paged_kv)
+        _check(self._lib.pka_run_noalloc(self._handle, _dev_ptr(q, "q", torch.bfloat16),
+                                         _dev_ptr(paged_kv, "paged_kv", torch.bfloat16),
+                                         _dev_ptr(o, "o"), _dev_ptr(lse, "lse", torch.float32),
+                                         _stream_ptr(stream)))
         return o, lse
 
     def run_ragged(self, q, k, v, o=None, lse=None, stream=None):

@@ -28,7 +28,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpka.so")
 HOST_LIB_PATH = os.path.join(HERE, "libpka_planner_host.so")
 ARCH = "gfx950"
-KERNELS = ["prefill.hip", "decode.hip", "merge.hip", "append.hip"]
+KERNELS = ["prefill.hip", "decode.hip", "merge.hip", "append.hip", "scratch.hip"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]

@@ -211,7 +211,7 @@ KvLayout standard_layout(const pka_plan* p) {
 }
 
 pka::AttnArgs attn_args(const pka_plan* p, const PartLaunch& part, const void* q, const void* k, const void* v,
-                        const KvLayout& kv, void* o, float* lse) {
+                        const KvLayout& kv, void* o, float* lse, void* float_base) {
   pka::AttnArgs a{};
   const int32_t* iw = static_cast<const int32_t*>(p->int_ws) + part.off_words;
   a.q = static_cast<const uint16_t*>(q);
@@ -219,7 +219,7 @@ pka::AttnArgs attn_args(const pka_plan* p, const PartLaunch& part, const void* q
   a.v = static_cast<const uint16_t*>(v);
   a.o = o;
   a.lse = lse;
-  a.part_o = reinterpret_cast<float*>(static_cast<char*>(p->float_ws) + part.float_off);
+  a.part_o = reinterpret_cast<float*>(static_cast<char*>(float_base) + part.float_off);
   a.ws = const_cast<int32_t*>(iw);
   const bool ragged = p->flags & PKA_RAGGED_KV;
   a.page_size = ragged ? 1 : p->page_size;
@@ -239,9 +239,9 @@ pka::AttnArgs attn_args(const pka_plan* p, const PartLaunch& part, const void* q
 
 // One part's attention launch and, if it split any KV, its merge.
 int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const void* k, const void* v,
-             const KvLayout& kv, void* o, float* lse, hipStream_t stream) {
+             const KvLayout& kv, void* o, float* lse, void* float_base, hipStream_t stream) {
   const bool stable = (p->flags & PKA_GRAPH_STABLE) != 0;
-  const pka::AttnArgs a = attn_args(p, part, q, k, v, kv, o, lse);
+  const pka::AttnArgs a = attn_args(p, part, q, k, v, kv, o, lse, float_base);
   const bool paged = !(p->flags & PKA_RAGGED_KV);
   hipError_t e;
   if (part.kernel == PKA_KERNEL_DECODE)
@@ -267,15 +267,18 @@ int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const voi
   return PKA_OK;
 }
 
+// float_base: where the plan's partial states go (its float workspace, or
+// the static scratch of pka_run_noalloc).
 int run_common(const pka_plan* p, const void* q, const void* k, const void* v, const KvLayout& kv, void* o,
-               float* lse, hipStream_t stream) {
+               float* lse, hipStream_t stream, void* float_base = nullptr) {
+  if (!float_base) float_base = p->float_ws;
   // A graph-stable plan always enqueues the same launches (a captured run is
   // replayed for later batches); the kernels find an empty batch empty.
   const bool stable = (p->flags & PKA_GRAPH_STABLE) != 0;
   if (p->info.total_q == 0 && !stable) return PKA_OK;
   if (!q || !o) return set_error(PKA_ERR_INVALID_ARG, "q and o must not be NULL");
   if (p->info.total_kv > 0 && !k) return set_error(PKA_ERR_INVALID_ARG, "KV pointer must not be NULL");
-  if (p->num_parts == 1) return run_part(p, p->parts[0], q, k, v, kv, o, lse, stream);
+  if (p->num_parts == 1) return run_part(p, p->parts[0], q, k, v, kv, o, lse, float_base, stream);
   // Mixed batch: the prefill launch goes first, on the caller's stream, so
   // that its workgroups take their compute units before the decode launch
   // (forked onto the plan's side stream) fills the rest; the caller's stream
@@ -284,9 +287,9 @@ int run_common(const pka_plan* p, const void* q, const void* k, const void* v, c
   if (e != hipSuccess) return hip_error("hipEventRecord(fork)", e);
   e = hipStreamWaitEvent(p->side, p->fork, 0);
   if (e != hipSuccess) return hip_error("hipStreamWaitEvent(fork)", e);
-  int st = run_part(p, p->parts[0], q, k, v, kv, o, lse, stream);
+  int st = run_part(p, p->parts[0], q, k, v, kv, o, lse, float_base, stream);
   if (st != PKA_OK) return st;
-  st = run_part(p, p->parts[1], q, k, v, kv, o, lse, p->side);
+  st = run_part(p, p->parts[1], q, k, v, kv, o, lse, float_base, p->side);
   if (st != PKA_OK) return st;
   e = hipEventRecord(p->join, p->side);
   if (e != hipSuccess) return hip_error("hipEventRecord(join)", e);
@@ -382,6 +385,24 @@ int pka_run(const pka_plan* plan, const void* q, const void* paged_kv, void* o, 
   const int64_t half = static_cast<int64_t>(plan->page_size) * plan->num_kv_heads * plan->head_dim;
   const void* v = paged_kv ? static_cast<const uint16_t*>(paged_kv) + half : nullptr;
   return run_common(plan, q, paged_kv, v, standard_layout(plan), o, lse, stream);
+}
+
+int pka_run_noalloc(const pka_plan* plan, const void* q, const void* paged_kv, void* o, float* lse,
+                    pka_stream_t stream) {
+  if (!plan_ok(plan)) return set_error(PKA_ERR_INVALID_ARG, "invalid plan");
+  if (plan->flags & PKA_RAGGED_KV)
+    return set_error(PKA_ERR_INVALID_ARG, "plan was made with PKA_RAGGED_KV: pka_run_noalloc takes a paged plan");
+  if (static_cast<size_t>(plan->info.float_ws_bytes) > pka::kNoallocScratchBytes)
+    return set_error(PKA_ERR_WORKSPACE, "pka_run_noalloc: the plan's partial states need " +
+                                            std::to_string(plan->info.float_ws_bytes) +
+                                            " bytes; the static scratch holds " +
+                                            std::to_string(pka::kNoallocScratchBytes));
+  void* scratch = nullptr;
+  const hipError_t e = pka::noalloc_scratch(&scratch);
+  if (e != hipSuccess) return hip_error("pka_run_noalloc: scratch address", e);
+  const int64_t half = static_cast<int64_t>(plan->page_size) * plan->num_kv_heads * plan->head_dim;
+  const void* v = paged_kv ? static_cast<const uint16_t*>(paged_kv) + half : nullptr;
+  return run_common(plan, q, paged_kv, v, standard_layout(plan), o, lse, stream, scratch);
 }
 
 int pka_run_paged_strided(const pka_plan* plan, const void* q, const void* k_cache, const void* v_cache,

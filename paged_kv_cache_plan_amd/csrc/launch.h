@@ -16,4 +16,10 @@ hipError_t launch_gather(const GatherArgs& a, int batch, hipStream_t stream);
 hipError_t launch_batch_indices_positions(const BatchPosArgs& a, hipStream_t stream);
 hipError_t launch_append(const AppendArgs& a, hipStream_t stream);
 
+// pka_run_noalloc: bytes of the static device scratch that holds a run's
+// split-KV partial states, and its address on the current device (looked up
+// once per device).
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+hipError_t noalloc_scratch(void** out);
+
 }  // namespace pka
