@@ -25,8 +25,9 @@
 //            rows as MFMA columns, so a lane holds 16 of a row's 32 scores per
 //            32-key block and the other 16 sit in lane l ^ 32.
 //   softmax  online, fp32, base 2 (sm_scale * log2 e folded into one FMA);
-//            row max needs one v_permlane32_swap; row sums stay per lane
-//            until the end.
+//            row max needs one v_permlane32_swap; the row sum adds the
+//            bf16-rounded p that multiply V, two per v_dot2, and stays per
+//            lane until the end.
 //   O^T     += V^T . P^T with the same MFMA; P^T is the S^T accumulator
 //            rounded to bf16 in place (no data movement), V^T comes from LDS.
 #include "args.h"
@@ -45,6 +46,12 @@ constexpr float kSlack = 8.f;
 constexpr int kSchedMfma = 0x008;
 constexpr int kSchedDsRead = 0x100;
 
+// lo + hi of a packed bf16 pair, added to acc in fp32 (v_dot2c_f32_bf16 with 1.0).
+__device__ __forceinline__ float sum_bf16x2(uint32_t x, float acc) {
+  typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+  const bf16x2 one = {static_cast<__bf16>(1.0f), static_cast<__bf16>(1.0f)};
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, x), one, acc, false);
+}
 // Position of key k (0..63) of a tile inside a V^T row.  Within each group of
 // 16 keys the order is 0-3, 8-11, 4-7, 12-15: exactly the key order in which
 // a lane of the S^T accumulator holds its scores, so P^T needs no shuffle.
@@ -379,29 +386,29 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
         const float m_new = bump ? m_tile : m_run;
         const float m_use = m_new == -INFINITY ? 0.f : m_new;
         const float alpha = (bump && m_run != -INFINITY) ? fast_exp2(m_run - m_new) : 1.f;
-        float rs = 0.f;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float p = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -m_use));
-            s[kb][i] = p;
-            rs += p;
-          }
-        l_run = l_run * alpha + rs;
-        m_run = m_new;
+          for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -m_use));
         if (__any(alpha != 1.f)) {  // the running max moved for some row of this wave
 #pragma unroll
           for (int b = 0; b < DB; ++b) o[b] *= alpha;
         }
 
-        // O^T += V^T . P^T, 16 keys per step
+        // O^T += V^T . P^T, 16 keys per step.  The row sum is taken from the
+        // same bf16-rounded p that multiply V, two per v_dot2 (each packed
+        // word is summed as its own value, before it joins the MFMA operand).
+        float rs = 0.f;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           const int kb = u >> 1, i0 = 8 * (u & 1);
           u32x4 pw;
 #pragma unroll
-          for (int w = 0; w < 4; ++w) pw[w] = pack_bf16(s[kb][i0 + 2 * w], s[kb][i0 + 2 * w + 1]);
+          for (int w = 0; w < 4; ++w) {
+            const uint32_t x = pack_bf16(s[kb][i0 + 2 * w], s[kb][i0 + 2 * w + 1]);
+            rs = sum_bf16x2(x, rs);
+            pw[w] = x;
+          }
           const bf16x8 pb = as_bf16x8(pw);
 #pragma unroll
           for (int b = 0; b < DB; ++b) {
@@ -411,6 +418,8 @@ __global__ __launch_bounds__(64 * prefill_waves(D), prefill_wg_per_cu(D)) void p
             o[b] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va, pb, o[b], 0, 0, 0);
           }
         }
+        l_run = l_run * alpha + rs;
+        m_run = m_new;
       }
       __syncthreads();
     }
