@@ -334,7 +334,7 @@ def bench_cascade(w, dev, steps, warmup, copies=2):
         flat.run(qs[i % copies], pools[i % copies], o, lse)
 
     def run_cascade(i):
-        casc.run(qs[i % copies], pools[i % copies])
+        casc.run(qs[i % copies], pools[i % copies], o, lse)
 
     res = {"kernel": "cascade", "plan_ms": plan_ms, "requests": w.batch, "prefix": w.notes["prefix"],
            "levels": len(w.notes["levels"])}

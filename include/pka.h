@@ -59,6 +59,9 @@ typedef struct ihipStream_t* pka_stream_t;
 /* Opaque plan, owned by the library (pka_plan_destroy frees it). */
 typedef struct pka_plan pka_plan;
 
+/* Opaque multi-level cascade, owned by the library (pka_cascade_destroy frees it). */
+typedef struct pka_cascade pka_cascade;
+
 enum {
   PKA_OK = 0,
   PKA_ERR_INVALID_ARG = 1, /* malformed arrays, null pointers, mismatched plan  */
@@ -329,6 +332,57 @@ int pka_append_paged_kv(const void* append_k, const void* append_v, const int32_
 int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_indptr,
                     const int32_t* kv_indices, const int32_t* kv_last_page_len, int32_t batch,
                     int32_t nnz_pages, pka_stream_t stream);
+
+/*
+ * Cascade attention (FlashInfer documentation, "flashinfer.cascade: Cascade
+ * Attention" and "Multi-level Cascade Inference Data Layout"): the query rows
+ * of a batch attend to keys stored in num_levels levels.  Level l groups the
+ * same total_q query rows into batch[l] contiguous groups (qo_indptr[l],
+ * batch[l] + 1 entries) that share the keys of that level's flat page table
+ * (kv_indptr[l], kv_indices[l], kv_last_page_len[l]; nnz_pages[l] ids), all
+ * in one paged_kv pool.  A query attends to the concatenation of its groups'
+ * keys, level 0 first, and the result equals attention over that
+ * concatenation (the recursive-attention identity: FlashInfer documentation,
+ * "Attention States and Recursive Attention").  Only the last level is
+ * causally masked (bottom-right, when causal != 0): the keys of the earlier
+ * levels precede every query of their groups, so each request's last-level
+ * group must hold at least its own query tokens (a causal last-level group
+ * with fewer keys than query rows is PKA_ERR_INVALID_ARG).
+ *
+ * Every level is planned like pka_plan_create (host arrays, validation,
+ * split-KV unless PKA_DISABLE_SPLIT_KV) into its share of the two
+ * caller-owned device workspaces; a run attends to each level into fp32
+ * states held in the float workspace and merges them (pka_merge_states) into
+ * o (bf16, or fp32 with PKA_OUT_FP32) and lse.  flags: PKA_OUT_FP32,
+ * PKA_DISABLE_SPLIT_KV; anything else is PKA_ERR_INVALID_ARG.  All levels must
+ * cover the same number of query rows (PKA_ERR_INVALID_ARG).
+ * pka_cascade_workspace_size reports the two workspace sizes (pure host,
+ * kv_indices not needed).  Ownership and stream rules are those of a plan:
+ * the workspaces must outlive the cascade and its runs, and the caller must
+ * make sure every run has completed before pka_cascade_destroy.  num_levels
+ * is at most 64.
+ */
+int pka_cascade_workspace_size(int32_t num_levels, const int32_t* const* qo_indptr,
+                               const int32_t* const* kv_indptr, const int32_t* const* kv_last_page_len,
+                               const int32_t* batch, int32_t num_qo_heads, int32_t num_kv_heads,
+                               int32_t head_dim, int32_t page_size, int32_t causal, uint32_t flags,
+                               size_t* int_ws_bytes, size_t* float_ws_bytes);
+
+int pka_cascade_create(int32_t num_levels, const int32_t* const* qo_indptr,
+                       const int32_t* const* kv_indptr, const int32_t* const* kv_indices,
+                       const int32_t* const* kv_last_page_len, const int32_t* batch,
+                       const int32_t* nnz_pages, int32_t num_pages_in_pool, int32_t num_qo_heads,
+                       int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
+                       float sm_scale, uint32_t flags, void* int_ws, size_t int_ws_bytes,
+                       void* float_ws, size_t float_ws_bytes, pka_stream_t stream, pka_cascade** out);
+
+/* Cascade attention of q bf16 [total_q, Hq, D] over paged_kv (layouts as
+ * pka_run) into o and lse (lse may be NULL).  Asynchronous on `stream`. */
+int pka_cascade_run(const pka_cascade* cascade, const void* q, const void* paged_kv, void* o,
+                    float* lse, pka_stream_t stream);
+
+/* Free a cascade and its level plans (NULL is a no-op). */
+void pka_cascade_destroy(pka_cascade* cascade);
 
 /* Free a plan.  The caller must first make sure every run using it has
  * completed (for example by synchronising the stream).  Its staging buffers

@@ -40,7 +40,8 @@ EXPORTED = ["pka_last_error", "pka_plan_workspace_size", "pka_plan_create", "pka
             "pka_plan_host_image", "pka_run", "pka_run_ragged", "pka_merge_states",
             "pka_debug_gather", "pka_plan_destroy", "pka_get_batch_indices_positions",
             "pka_append_paged_kv", "pka_run_paged_strided", "pka_merge_states_strided",
-            "pka_plan_update", "pka_run_noalloc"]
+            "pka_plan_update", "pka_run_noalloc", "pka_cascade_workspace_size", "pka_cascade_create",
+            "pka_cascade_run", "pka_cascade_destroy"]
 
 
 class PlanInfo(ctypes.Structure):
@@ -103,6 +104,11 @@ def load_library(path: Optional[str] = None):
         "pka_append_paged_kv": (c_int, [vp, vp, vp, vp, i32, vp, i32, i32, i32, i32, vp, vp, i32, vp]),
         "pka_plan_update": (c_int, [vp, i32p, i32p, i32p, i32p, i32, i32, vp]),
         "pka_plan_destroy": (None, [vp]),
+        "pka_cascade_workspace_size": (c_int, [i32, vp, vp, vp, vp, i32, i32, i32, i32, i32, u32, szp, szp]),
+        "pka_cascade_create": (c_int, [i32, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, u32, vp, sz,
+                                       vp, sz, vp, ctypes.POINTER(vp)]),
+        "pka_cascade_run": (c_int, [vp, vp, vp, vp, vp, vp]),
+        "pka_cascade_destroy": (None, [vp]),
     }
     for name, (res, args) in sigs.items():
         try:
@@ -444,51 +450,125 @@ def merge_states_levels(v, s, out_fp32=False, stream=None):
     return v_out, s_out
 
 
+class _LevelArrays:
+    pass
+
+
+def _level_arrays(levels):
+    """Host int32 copies of every level's four arrays, kept alive on the
+    returned object, with the int32* [num_levels] pointer arrays and the
+    per-level batch and nnz_pages counts that pka_cascade_* take."""
+    import torch
+    n = len(levels)
+    r = _LevelArrays()
+    names = ("qo_indptr", "kv_indptr", "kv_indices", "kv_last_page_len")
+    for k, name in enumerate(names):
+        ts, arr = [], (ctypes.POINTER(ctypes.c_int32) * max(n, 1))()
+        for i, lev in enumerate(levels):
+            if len(lev) != 4:
+                raise ValueError("a level is (qo_indptr, kv_indptr, kv_indices, kv_last_page_len)")
+            t, ptr = _host_i32(lev[k])
+            ts.append(t)
+            arr[i] = ptr
+        setattr(r, name, ts)
+        setattr(r, ("qo", "kvp", "kvi", "last")[k], arr)
+    r.batch = (ctypes.c_int32 * max(n, 1))(*[t.numel() - 1 for t in r.qo_indptr])
+    r.nnz = (ctypes.c_int32 * max(n, 1))(*[t.numel() for t in r.kv_indices])
+    return r
+
+
+def cascade_workspace_size(levels, num_qo_heads, num_kv_heads, head_dim, page_size, causal=True, out_fp32=False,
+                           disable_split_kv=False):
+    """(int_ws_bytes, float_ws_bytes) a cascade over ``levels`` needs
+    (pka_cascade_workspace_size: host only, no GPU)."""
+    L = load_library()
+    lv = _level_arrays(levels)
+    flags = (PKA_OUT_FP32 if out_fp32 else 0) | (PKA_DISABLE_SPLIT_KV if disable_split_kv else 0)
+    a, b = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(L.pka_cascade_workspace_size(len(levels), lv.qo, lv.kvp, lv.last, lv.batch, num_qo_heads, num_kv_heads,
+                                        head_dim, page_size, int(bool(causal)), flags, ctypes.byref(a),
+                                        ctypes.byref(b)))
+    return a.value, b.value
+
+
 class Cascade:
-    """Multi-level cascade attention over one paged KV pool (FlashInfer
-    documentation, "flashinfer.cascade: Cascade Attention" and "Multi-level
-    Cascade Inference Data Layout").
+    """Multi-level cascade attention over one paged KV pool (pka_cascade_*;
+    FlashInfer documentation, "flashinfer.cascade: Cascade Attention" and
+    "Multi-level Cascade Inference Data Layout").
 
     ``levels`` is a list of (qo_indptr, kv_indptr, kv_indices,
-    kv_last_page_len): level l groups the same total_q query rows into
-    contiguous groups (its qo_indptr) that share the keys of its page table.
-    A query attends to the concatenation of its groups' keys, level 0 first.
-    Only the last level is masked (bottom-right causal when ``causal``); the
-    keys of earlier levels precede every query, so each request's last-level
-    keys must include its own query tokens (at least qo_len keys).  Each level is one plan and
-    run writing an fp32 state into a [levels, total_q, Hq, D] buffer, and
-    pka_merge_states_strided merges them (the recursive-attention identity).
+    kv_last_page_len) host arrays: level l groups the same total_q query rows
+    into contiguous groups (its qo_indptr) that share the keys of its page
+    table.  A query attends to the concatenation of its groups' keys, level 0
+    first; only the last level is masked (bottom-right causal when
+    ``causal``), so each request's last-level keys must include its own query
+    tokens.  The library plans every level into its share of the two device
+    workspaces allocated here, and a run merges the levels' states.
     """
 
     def __init__(self, levels, num_qo_heads, num_kv_heads, head_dim, page_size, causal=True, sm_scale=-1.0,
-                 num_pages=None, out_fp32=False, device=None, stream=None):
+                 num_pages=None, out_fp32=False, disable_split_kv=False, device=None, stream=None):
+        import torch
+        L = load_library()
+        self._lib = L
+        self._handle = ctypes.c_void_p()
         n = len(levels)
         if n < 1:
             raise ValueError("at least one level")
-        self.plans = []
-        for i, (qo, kvp, kvi, last) in enumerate(levels):
-            self.plans.append(Plan(qo, kvp, kvi, last, num_qo_heads, num_kv_heads, head_dim, page_size,
-                                   causal=causal and i == n - 1, sm_scale=sm_scale, num_pages=num_pages,
-                                   out_fp32=True, device=device, stream=stream))
-        totals = {p.total_q for p in self.plans}
-        if len(totals) != 1:
-            raise ValueError("every level must cover the same query rows")
-        self.total_q = totals.pop()
+        dev = torch.device(device) if device is not None else torch.device("cuda", torch.cuda.current_device())
+        if dev.type != "cuda":
+            raise ValueError("Cascade needs a GPU device")
+        lv = _level_arrays(levels)
+        if num_pages is None:
+            num_pages = max((int(t.max()) + 1 for t in lv.kv_indices if t.numel()), default=0)
+        flags = (PKA_OUT_FP32 if out_fp32 else 0) | (PKA_DISABLE_SPLIT_KV if disable_split_kv else 0)
+        a, b = ctypes.c_size_t(), ctypes.c_size_t()
+        _check(L.pka_cascade_workspace_size(n, lv.qo, lv.kvp, lv.last, lv.batch, num_qo_heads, num_kv_heads, head_dim,
+                                            page_size, int(bool(causal)), flags, ctypes.byref(a), ctypes.byref(b)))
+        self.int_ws = torch.empty(max(a.value, 256), dtype=torch.uint8, device=dev)
+        self.float_ws = torch.empty(max(b.value, 256), dtype=torch.uint8, device=dev)
+        self._stream = stream if stream is not None else torch.cuda.current_stream(dev)
+        _check(L.pka_cascade_create(n, lv.qo, lv.kvp, lv.kvi, lv.last, lv.batch, lv.nnz, int(num_pages), num_qo_heads,
+                                    num_kv_heads, head_dim, page_size, int(bool(causal)),
+                                    float(sm_scale) if sm_scale and sm_scale > 0 else 0.0, flags,
+                                    ctypes.c_void_p(self.int_ws.data_ptr()), self.int_ws.numel(),
+                                    ctypes.c_void_p(self.float_ws.data_ptr()), self.float_ws.numel(),
+                                    _stream_ptr(self._stream), ctypes.byref(self._handle)))
+        self.total_q = int(lv.qo_indptr[0][-1]) if lv.qo_indptr[0].numel() else 0
         self.num_qo_heads, self.head_dim, self.out_fp32 = num_qo_heads, head_dim, out_fp32
+        self.device = dev
 
-    def run(self, q, paged_kv, stream=None):
+    def run(self, q, paged_kv, o=None, lse=None, stream=None):
         """Returns (o, lse) of the cascade."""
         import torch
-        S = len(self.plans)
-        v = torch.empty((S, self.total_q, self.num_qo_heads, self.head_dim), dtype=torch.float32, device=q.device)
-        s = torch.empty((S, self.total_q, self.num_qo_heads), dtype=torch.float32, device=q.device)
-        for i, p in enumerate(self.plans):
-            p.run(q, paged_kv, o=v[i], lse=s[i], stream=stream)
-        return merge_states_levels(v, s, out_fp32=self.out_fp32, stream=stream)
+        shape = (self.total_q, self.num_qo_heads, self.head_dim)
+        if o is None:
+            o = torch.empty(shape, dtype=torch.float32 if self.out_fp32 else torch.bfloat16, device=q.device)
+        if lse is None:
+            lse = torch.empty(shape[:2], dtype=torch.float32, device=q.device)
+        if tuple(q.shape) != shape or q.dtype != torch.bfloat16:
+            raise ValueError(f"q must be bf16 {list(shape)}, got {q.dtype} {tuple(q.shape)}")
+        if tuple(o.shape) != shape or o.dtype != (torch.float32 if self.out_fp32 else torch.bfloat16):
+            raise ValueError("o does not match the cascade's output shape and dtype")
+        if tuple(lse.shape) != shape[:2] or lse.dtype != torch.float32:
+            raise ValueError("lse must be float32 [total_q, Hq]")
+        _check(self._lib.pka_cascade_run(self._handle, _dev_ptr(q, "q", torch.bfloat16),
+                                         _dev_ptr(paged_kv, "paged_kv", torch.bfloat16), _dev_ptr(o, "o"),
+                                         _dev_ptr(lse, "lse", torch.float32), _stream_ptr(stream)))
+        return o, lse
 
     def close(self):
-        for p in self.plans:
-            p.close()
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            import torch
+            torch.cuda.synchronize(self.device)
+            self._lib.pka_cascade_destroy(self._handle)
+            self._handle = ctypes.c_void_p()
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def get_batch_indices_positions(append_indptr, seq_lens, nnz, stream=None):

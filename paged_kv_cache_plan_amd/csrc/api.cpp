@@ -35,7 +35,8 @@ int hip_error(const char* what, hipError_t e) {
   return set_error(PKA_ERR_HIP, std::string(what) + ": " + hipGetErrorString(e));
 }
 
-constexpr uint32_t kPlanMagic = 0x4e4c5050u;  // "PPLN"
+constexpr uint32_t kPlanMagic = 0x4e4c5050u;     // "PPLN"
+constexpr uint32_t kCascadeMagic = 0x43534350u;  // "PCSC"
 
 int env_int(const char* name) {
   const char* s = std::getenv(name);
@@ -129,6 +130,18 @@ struct pka_plan {
   // back into the caller's stream with the two events.
   hipStream_t side;
   hipEvent_t fork, join;
+};
+
+// A cascade: one plan per level over its share of the workspaces, and the
+// levels' fp32 states merged into the output.
+struct pka_cascade {
+  uint32_t magic;
+  int32_t num_levels, num_qo_heads, head_dim;
+  int64_t total_q;
+  uint32_t flags;
+  std::vector<pka_plan*> plans;
+  float* states_v;
+  float* states_s;
 };
 
 namespace {
@@ -584,6 +597,79 @@ int pka_plan_update(pka_plan* plan, const int32_t* qo_indptr, const int32_t* kv_
   } catch (const std::exception& ex) {
     return set_error(PKA_ERR_INVALID_ARG, ex.what());
   }
+}
+
+int pka_cascade_create(int32_t num_levels, const int32_t* const* qo_indptr, const int32_t* const* kv_indptr,
+                       const int32_t* const* kv_indices, const int32_t* const* kv_last_page_len, const int32_t* batch,
+                       const int32_t* nnz_pages, int32_t num_pages_in_pool, int32_t num_qo_heads, int32_t num_kv_heads,
+                       int32_t head_dim, int32_t page_size, int32_t causal, float sm_scale, uint32_t flags, void* int_ws,
+                       size_t int_ws_bytes, void* float_ws, size_t float_ws_bytes, pka_stream_t stream,
+                       pka_cascade** out) {
+  try {
+    if (!out) return set_error(PKA_ERR_INVALID_ARG, "out must not be NULL");
+    *out = nullptr;
+    if (!int_ws || !float_ws) return set_error(PKA_ERR_INVALID_ARG, "workspaces must not be NULL");
+    if (!kv_indices || !nnz_pages) return set_error(PKA_ERR_INVALID_ARG, "cascade: kv_indices and nnz_pages must not be NULL");
+    pka::CascadeLayout lay;
+    int st = pka::cascade_layout(num_levels, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, batch, nnz_pages,
+                                 num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size, causal, flags,
+                                 &lay);
+    if (st != PKA_OK) return st;
+    if (int_ws_bytes < lay.int_total || float_ws_bytes < lay.float_total)
+      return set_error(PKA_ERR_WORKSPACE, "cascade workspaces have " + std::to_string(int_ws_bytes) + " / " +
+                                              std::to_string(float_ws_bytes) + " bytes, need " +
+                                              std::to_string(lay.int_total) + " / " + std::to_string(lay.float_total));
+    pka_cascade* c = new pka_cascade{};
+    c->magic = kCascadeMagic;
+    c->num_levels = num_levels;
+    c->num_qo_heads = num_qo_heads;
+    c->head_dim = head_dim;
+    c->total_q = lay.total_q;
+    c->flags = flags;
+    c->states_v = reinterpret_cast<float*>(static_cast<char*>(float_ws) + lay.states_v);
+    c->states_s = reinterpret_cast<float*>(static_cast<char*>(float_ws) + lay.states_s);
+    for (int l = 0; l < num_levels; ++l) {
+      pka_plan* p = nullptr;
+      st = pka_plan_create(qo_indptr[l], kv_indptr[l], kv_indices[l], kv_last_page_len[l], batch[l], nnz_pages[l],
+                           num_pages_in_pool, num_qo_heads, num_kv_heads, head_dim, page_size,
+                           (causal && l == num_levels - 1) ? 1 : 0, sm_scale,
+                           (flags & PKA_DISABLE_SPLIT_KV) | pka::kCascadeLevelFlags,
+                           static_cast<char*>(int_ws) + lay.int_off[l], lay.int_bytes[l],
+                           static_cast<char*>(float_ws) + lay.float_off[l], lay.float_bytes[l], stream, &p);
+      if (st != PKA_OK) {
+        const std::string msg = std::string("cascade: level ") + std::to_string(l) + ": " + pka_last_error();
+        pka_cascade_destroy(c);
+        return set_error(st, msg);
+      }
+      c->plans.push_back(p);
+    }
+    *out = c;
+    return PKA_OK;
+  } catch (const std::exception& ex) {
+    return set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
+
+int pka_cascade_run(const pka_cascade* c, const void* q, const void* paged_kv, void* o, float* lse,
+                    pka_stream_t stream) {
+  if (!c || c->magic != kCascadeMagic) return set_error(PKA_ERR_INVALID_ARG, "invalid cascade");
+  if (c->total_q == 0) return PKA_OK;
+  if (!o) return set_error(PKA_ERR_INVALID_ARG, "o must not be NULL");
+  const int64_t n = c->total_q, H = c->num_qo_heads, D = c->head_dim;
+  for (int l = 0; l < c->num_levels; ++l) {
+    const int st = pka_run(c->plans[l], q, paged_kv, c->states_v + l * n * H * D, c->states_s + l * n * H, stream);
+    if (st != PKA_OK) return st;
+  }
+  // state s of row i, head h: v[i*H*D + s*n*H*D + h*D ..], s[i*H + s*n*H + h]
+  return pka_merge_states_strided(c->states_v, c->states_s, n, c->num_levels, c->num_qo_heads, c->head_dim, H * D,
+                                  n * H * D, H, n * H, o, lse, c->flags & PKA_OUT_FP32, stream);
+}
+
+void pka_cascade_destroy(pka_cascade* c) {
+  if (!c || c->magic != kCascadeMagic) return;
+  for (pka_plan* p : c->plans) pka_plan_destroy(p);
+  c->magic = 0;
+  delete c;
 }
 
 void pka_plan_destroy(pka_plan* plan) {

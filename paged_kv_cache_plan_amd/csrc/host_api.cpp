@@ -155,9 +155,89 @@ void fill_plan_info(const Planned& pl, int32_t batch, int32_t nnz, pka_plan_info
   info->decode_cus = mp.decode_cus;
 }
 
+int cascade_layout(int32_t num_levels, const int32_t* const* qo_indptr, const int32_t* const* kv_indptr,
+                   const int32_t* const* kv_indices, const int32_t* const* kv_last_page_len, const int32_t* batch,
+                   const int32_t* nnz_pages, int32_t num_pages, int32_t num_qo_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t page_size, int32_t causal, uint32_t flags, CascadeLayout* out) {
+  if (num_levels < 1 || num_levels > 64) return set_error(PKA_ERR_INVALID_ARG, "cascade: num_levels must be in [1, 64]");
+  if (!qo_indptr || !kv_indptr || !kv_last_page_len || !batch)
+    return set_error(PKA_ERR_INVALID_ARG, "cascade: level arrays must not be NULL");
+  if (flags & ~kCascadeFlags)
+    return set_error(PKA_ERR_INVALID_ARG, "cascade: only PKA_OUT_FP32 and PKA_DISABLE_SPLIT_KV are accepted");
+  *out = CascadeLayout{};
+  auto align = [](size_t x) { return (x + 255) / 256 * 256; };
+  size_t ioff = 0, foff = 0;
+  for (int l = 0; l < num_levels; ++l) {
+    if (!qo_indptr[l] || !kv_indptr[l] || batch[l] < 0)
+      return set_error(PKA_ERR_INVALID_ARG, "cascade: level " + std::to_string(l) + " has a NULL array");
+    const int32_t nnz = kv_indptr[l][batch[l]];
+    if (nnz_pages && nnz_pages[l] != nnz)
+      return set_error(PKA_ERR_INVALID_ARG, "cascade: level " + std::to_string(l) + ": kv_indptr[batch] = " +
+                                                std::to_string(nnz) + " but nnz_pages = " + std::to_string(nnz_pages[l]));
+    // Only the last level is causally masked: the keys of the earlier
+    // levels precede every query of their groups.
+    const uint32_t lflags = (flags & PKA_DISABLE_SPLIT_KV) | kCascadeLevelFlags;
+    PlanInput in = make_input(qo_indptr[l], kv_indptr[l], kv_indices ? kv_indices[l] : nullptr, kv_last_page_len[l],
+                              batch[l], nnz, num_pages, num_qo_heads, num_kv_heads, head_dim, page_size,
+                              (causal && l == num_levels - 1) ? 1 : 0, lflags, kv_indices != nullptr);
+    Planned pl;
+    const int st = plan_or_error(in, &pl);
+    if (st != PKA_OK) return set_error(st, "cascade: level " + std::to_string(l) + ": " + pka_last_error());
+    if (causal && l == num_levels - 1) {
+      // The earlier levels' keys precede every query, so the causal mask of
+      // the whole concatenation is the last level's own bottom-right mask
+      // only if each of its groups holds at least its own query rows.
+      for (int32_t g = 0; g < batch[l]; ++g) {
+        const int64_t pages = kv_indptr[l][g + 1] - kv_indptr[l][g];
+        const int64_t keys = pages == 0 ? 0 : (pages - 1) * page_size + kv_last_page_len[l][g];
+        const int64_t rows = qo_indptr[l][g + 1] - qo_indptr[l][g];
+        if (keys < rows)
+          return set_error(PKA_ERR_INVALID_ARG, "cascade: last level, group " + std::to_string(g) + " has " +
+                                                    std::to_string(keys) + " keys for " + std::to_string(rows) +
+                                                    " causal query rows");
+      }
+    }
+    const int64_t tq = qo_indptr[l][batch[l]];
+    if (l == 0) out->total_q = tq;
+    else if (tq != out->total_q)
+      return set_error(PKA_ERR_INVALID_ARG, "cascade: level " + std::to_string(l) + " covers " + std::to_string(tq) +
+                                                " query rows, level 0 covers " + std::to_string(out->total_q));
+    out->int_off.push_back(ioff);
+    out->int_bytes.push_back(pl.image().size() * sizeof(int32_t));
+    out->float_off.push_back(foff);
+    out->float_bytes.push_back(pl.float_ws_bytes());
+    ioff = align(ioff + out->int_bytes.back());
+    foff = align(foff + out->float_bytes.back());
+  }
+  const size_t rows = static_cast<size_t>(out->total_q) * num_qo_heads;
+  out->states_v = foff;
+  out->states_s = align(foff + static_cast<size_t>(num_levels) * rows * head_dim * sizeof(float));
+  out->float_total = align(out->states_s + static_cast<size_t>(num_levels) * rows * sizeof(float));
+  out->int_total = ioff;
+  return PKA_OK;
+}
+
 }  // namespace pka
 
 extern "C" {
+
+int pka_cascade_workspace_size(int32_t num_levels, const int32_t* const* qo_indptr, const int32_t* const* kv_indptr,
+                               const int32_t* const* kv_last_page_len, const int32_t* batch, int32_t num_qo_heads,
+                               int32_t num_kv_heads, int32_t head_dim, int32_t page_size, int32_t causal,
+                               uint32_t flags, size_t* int_ws_bytes, size_t* float_ws_bytes) {
+  try {
+    if (!int_ws_bytes || !float_ws_bytes) return pka::set_error(PKA_ERR_INVALID_ARG, "null size pointer");
+    pka::CascadeLayout lay;
+    const int st = pka::cascade_layout(num_levels, qo_indptr, kv_indptr, nullptr, kv_last_page_len, batch, nullptr, 0,
+                                       num_qo_heads, num_kv_heads, head_dim, page_size, causal, flags, &lay);
+    if (st != PKA_OK) return st;
+    *int_ws_bytes = lay.int_total;
+    *float_ws_bytes = lay.float_total;
+    return PKA_OK;
+  } catch (const std::exception& ex) {
+    return pka::set_error(PKA_ERR_INVALID_ARG, ex.what());
+  }
+}
 
 const char* pka_last_error(void) { return pka::g_last_error.c_str(); }
 

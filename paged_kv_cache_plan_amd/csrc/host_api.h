@@ -42,4 +42,27 @@ int plan_for_create(const PlanInput& in, Planned* res);
 
 void fill_plan_info(const Planned& pl, int32_t batch, int32_t nnz, pka_plan_info* info);
 
+// Where a cascade keeps its parts: level l's plan workspaces at
+// int_off[l] / float_off[l] (bytes, 256-aligned) inside the caller's two
+// workspaces, then, in the float workspace, the levels' fp32 states
+// v [L, total_q, Hq, D] at states_v and s [L, total_q, Hq] at states_s.
+struct CascadeLayout {
+  std::vector<size_t> int_off, int_bytes, float_off, float_bytes;
+  size_t states_v = 0, states_s = 0;
+  size_t int_total = 0, float_total = 0;
+  int64_t total_q = 0;
+};
+
+// The flags a cascade passes to its level plans: fp32 states, split-KV as
+// the caller asked.
+constexpr uint32_t kCascadeLevelFlags = PKA_OUT_FP32;
+constexpr uint32_t kCascadeFlags = PKA_OUT_FP32 | PKA_DISABLE_SPLIT_KV;
+
+// Validate the levels (same query rows on every level) and size the
+// workspaces; kv_indices may be null (sizes only).
+int cascade_layout(int32_t num_levels, const int32_t* const* qo_indptr, const int32_t* const* kv_indptr,
+                   const int32_t* const* kv_indices, const int32_t* const* kv_last_page_len, const int32_t* batch,
+                   const int32_t* nnz_pages, int32_t num_pages, int32_t num_qo_heads, int32_t num_kv_heads,
+                   int32_t head_dim, int32_t page_size, int32_t causal, uint32_t flags, CascadeLayout* out);
+
 }  // namespace pka

@@ -1,7 +1,8 @@
-"""Cascade attention (pka.Cascade: one plan and run per level, merged by
-pka_merge_states_strided) against the oracle run on the concatenation of each
-request's keys, level 0 first, with the bottom-right causal mask over the
-whole length -- the recursive-attention identity says the two agree."""
+"""Cascade attention (pka.Cascade over pka_cascade_create / pka_cascade_run:
+one plan per level, the levels' states merged on the GPU) against the oracle
+run on the concatenation of each request's keys, level 0 first, with the
+bottom-right causal mask over the whole length -- the recursive-attention
+identity says the two agree."""
 import pytest
 import torch
 
