@@ -81,6 +81,15 @@ def test_product_never_imports_the_input_generator():
             assert "inputs" not in _imports(os.path.join(pkg, f)), f
 
 
+def test_oracle_never_imports_the_input_generator():
+    """The oracle takes its inputs as arguments: it shares nothing with the
+    generator that draws them."""
+    odir = os.path.join(ROOT, "oracle")
+    for f in os.listdir(odir):
+        if f.endswith(".py"):
+            assert "inputs" not in _imports(os.path.join(odir, f)), f
+
+
 # ---------------------------------------------------------------------------
 # Run arguments are checked against the plan before any pointer is passed
 # ---------------------------------------------------------------------------
