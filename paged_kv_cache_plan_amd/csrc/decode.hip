@@ -113,14 +113,23 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
     vb_ptr = a.v + U.hk * a.head_stride;
   };
 
-  // V loader: lane handles chunk vc of the 8 keys in slot group vg.
-  const int vc = lane % CPR, vg = lane / CPR;
-  const bool v_lane = vg < 4;
+  // V loader: a V^T row (one d, 32 keys) holds four 8-key slots; slot vg
+  // holds keys 4 vg + j (j < 4) and 16 + 4 vg + j - 4 (j >= 4).  At D=128
+  // (16 chunks a row) lane (vc, vg) loads chunk vc of all 8 keys of slot vg;
+  // at D=64 (8 chunks a row) lane (vc, vh, vg) loads chunk vc of the half vh
+  // of slot vg (VJ = 4 keys), so that every lane loads only rows it uses.
+  constexpr int VJ = CPR == 16 ? 8 : 4;
+  static_assert(CPR == 16 || CPR == 8, "head_dim 128 or 64");
+  const int vc = lane % CPR;
+  const int vg = (lane / CPR) & 3, vh = CPR == 16 ? 0 : lane / (4 * CPR);
   uint16_t* vt = reinterpret_cast<uint16_t*>(smem) + wave * VT_ELEMS;
 
   // Keys of one step handled by this lane: K rows 16 kb + col (kb = 0, 1);
-  // V rows for slot 8 vg + j: 4 vg + j (j < 4), 16 + 4 vg + j - 4 (j >= 4).
-  auto v_key = [&](int j) { return j < 4 ? 4 * vg + j : 16 + 4 * vg + (j - 4); };
+  // V rows: element j of the lane's part of slot vg.
+  auto v_key = [&](int j) {
+    const int jj = j + 4 * vh;
+    return jj < 4 ? 4 * vg + jj : 16 + 4 * vg + (jj - 4);
+  };
 
   // Page ids of a step.
   struct IdsUniform { int s[2]; };
@@ -162,7 +171,7 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
       return static_cast<int64_t>(kv_base + key) * a.page_stride;
     }
   };
-  struct Data { u32x4 k[2][DS]; u32x4 v[8]; };
+  struct Data { u32x4 k[2][DS]; u32x4 v[VJ]; };
   auto fetch_data = [&](int k0, const Ids& id, Data& x) {
     const int last = kv_hi - 1;
 #pragma unroll
@@ -176,12 +185,12 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
       for (int s = 0; s < DS; ++s) x.k[kb][s] = ld16_stream(p + 32 * s);
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < VJ; ++j) {
       const int key = min(k0 + v_key(j), last);
       int pid = 0;
-      if constexpr (MODE == kPagedUniform) pid = id.s[j >> 2];
+      if constexpr (MODE == kPagedUniform) pid = (j + 4 * vh) < 4 ? id.s[0] : id.s[1];  // key half of the step
       if constexpr (LANE) pid = __builtin_amdgcn_ds_bpermute(v_key(j) * 4, id.key);
-      x.v[j] = ld16_stream(vb_ptr + row_off(key, pid) + 8 * vc);  // lanes past the 4 V groups load and ignore
+      x.v[j] = ld16_stream(vb_ptr + row_off(key, pid) + 8 * vc);
     }
   };
 
@@ -254,18 +263,26 @@ __global__ __launch_bounds__(kThreads, kDecodeWgPerCu) void decode_kernel(AttnAr
     // sees these loads as still pending: a later write to their registers
     // would wait for the newest loads)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) __asm__ volatile("" ::"v"(cur.v[j]));
-    if (v_lane) {
+    for (int j = 0; j < VJ; ++j) __asm__ volatile("" ::"v"(cur.v[j]));
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int d = 8 * vc + e;
-        const int w = e >> 1;
+    for (int e = 0; e < 8; ++e) {
+      const int d = 8 * vc + e;
+      const int w = e >> 1;
+      uint16_t* dst = vt + d * kTK + ((vg ^ dvt_swz(d)) * 8) + 4 * vh;
+      if constexpr (VJ == 8) {
         u32x4 pk;
 #pragma unroll
         for (int h = 0; h < 4; ++h)
           pk[h] = (e & 1) ? pack_hi16(cur.v[2 * h][w], cur.v[2 * h + 1][w])
                           : pack_lo16(cur.v[2 * h][w], cur.v[2 * h + 1][w]);
-        st16(vt + d * kTK + ((vg ^ dvt_swz(d)) * 8), pk);
+        st16(dst, pk);
+      } else {
+        u32x2 pk;
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+          pk[h] = (e & 1) ? pack_hi16(cur.v[2 * h][w], cur.v[2 * h + 1][w])
+                          : pack_lo16(cur.v[2 * h][w], cur.v[2 * h + 1][w]);
+        *reinterpret_cast<u32x2*>(dst) = pk;
       }
     }
     __asm__ volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
