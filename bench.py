@@ -479,6 +479,77 @@ def clock_under_load(launch, n):
     return mhz
 
 
+TRAFFIC_WORKLOADS = ["dense_vs_sparse_paged", "long_causal", "batch_decode", "append"]
+COPY_CALIBRATION_BYTES = 1 << 30  # --copy-calibration copies 2^28 floats
+
+
+def _counter_means(path):
+    """Mean counter value (KiB) per kernel over the dispatches of one
+    rocprofv3 --pmc CSV (one counter per run)."""
+    import csv
+    sums, counts = {}, {}
+    with open(path) as f:
+        for r in csv.DictReader(f):
+            k = r["Kernel_Name"]
+            sums[k] = sums.get(k, 0.0) + float(r["Counter_Value"])
+            counts[k] = counts.get(k, 0) + 1
+    return {k: sums[k] / counts[k] for k in sums}
+
+
+def _short_kernel(name):
+    n = name.replace("void ", "").replace("pka::(anonymous namespace)::", "")
+    return n.split("(pka::")[0]
+
+
+def summarize_traffic(prof_dir):
+    """profiles/traffic.json from rocprofv3 FETCH_SIZE / WRITE_SIZE runs
+    (directories pmc_<COUNTER>_<workload> and pmc_<COUNTER>_calib under
+    prof_dir): each counter is scaled by what it reads for a plain copy of
+    known size, and a workload's bytes per launch sum its attention kernels."""
+    import glob
+
+    def means(counter, tag):
+        files = glob.glob(os.path.join(prof_dir, f"pmc_{counter}_{tag}", "*counter_collection.csv"))
+        return _counter_means(files[0]) if files else {}
+
+    factors = {}
+    for counter in ("FETCH_SIZE", "WRITE_SIZE"):
+        copy = [v for k, v in means(counter, "calib").items() if "copyBuffer" in k or "copy" in k.lower()]
+        factors[counter] = (COPY_CALIBRATION_BYTES / 1024) / copy[0]
+    out = {"kernel_source_hash": kernel_source_hash(), "fetch_factor": factors["FETCH_SIZE"],
+           "write_factor": factors["WRITE_SIZE"], "detail": {}}
+    lines = []
+    for w in TRAFFIC_WORKLOADS:
+        fetch, write = means("FETCH_SIZE", w), means("WRITE_SIZE", w)
+        det, total = {}, 0.0
+        for k in sorted(set(fetch) | set(write)):
+            fb = fetch.get(k, 0.0) * 1024 * factors["FETCH_SIZE"]
+            wb = write.get(k, 0.0) * 1024 * factors["WRITE_SIZE"]
+            det[_short_kernel(k)] = {"fetch_bytes": fb, "write_bytes": wb}
+            total += fb + wb
+            lines.append(f"{w:22s} {_short_kernel(k)[:34]:34s} fetch {fetch.get(k, 0.0):12.1f} KiB -> {fb / 1e6:9.1f} MB"
+                         f"   write {write.get(k, 0.0):11.1f} KiB -> {wb / 1e6:8.1f} MB")
+        out["detail"][w] = det
+        out[w] = total
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    return out, lines
+
+
+def summarize_trace(csv_path, pattern):
+    """avg/min/max duration of the kernels matching `pattern` in a rocprofv3
+    --kernel-trace --stats kernel_stats.csv."""
+    import csv
+    import re
+    rows = []
+    with open(csv_path) as f:
+        for r in csv.DictReader(f):
+            if re.search(pattern, r["Name"]):
+                rows.append((_short_kernel(r["Name"]), int(r["Calls"]), float(r["AverageNs"]), float(r["MinNs"]),
+                             float(r["MaxNs"])))
+    return rows
+
+
 def load_traffic():
     path = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(path):
@@ -522,7 +593,14 @@ def main():
     ap.add_argument("--no-clock", action="store_true", help="skip the rocm-smi clock reading")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--summarize-traffic", metavar="DIR", default=None,
+                    help="write profiles/traffic.json from rocprofv3 FETCH_SIZE/WRITE_SIZE runs under DIR (no GPU)")
     args = ap.parse_args()
+    if args.summarize_traffic:
+        out, lines = summarize_traffic(args.summarize_traffic)
+        print("fetch factor %.4f, write factor %.4f" % (out["fetch_factor"], out["write_factor"]))
+        print("\n".join(lines))
+        return
     WARM_MS = args.warm_ms
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
