@@ -85,7 +85,9 @@ def test_dense_vs_vector_sparse_full():
     d_o = (o_p - o_r).abs().max().item()
     d_l = (l_p - l_r).abs().max().item()
     assert d_o <= 2e-2 and d_l <= 1e-2, (d_o, d_l)
+    print(f"dense_vs_sparse: paged vs ragged on every row: max |dO| {d_o:.2e}, max |dlse| {d_l:.2e}", flush=True)
     _check_sampled(w, o_p, l_p, 2048, 21, "dense_vs_sparse paged")
+    _check_sampled(w, o_r, l_r, 512, 24, "dense_vs_sparse ragged")
 
 
 def test_gqa_append_full():

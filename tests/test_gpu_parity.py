@@ -17,7 +17,8 @@ def test_tiny_causal_paged(out_fp32):
     w = W.tiny()
     o, lse, info = run_paged(w, out_fp32=out_fp32)
     ref_o, ref_l = oracle_paged(w)
-    compare(o, lse, ref_o, ref_l, "tiny")
+    err = compare(o, lse, ref_o, ref_l, "tiny")
+    print(f"tiny (out_fp32={out_fp32}): max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
     assert info["kernel"] == pka.PKA_KERNEL_PREFILL
 
 
