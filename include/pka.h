@@ -84,7 +84,8 @@ enum {
 #define PKA_MIXED_BATCH 0x10u     /* a batch with both prefill requests (qo_len > 1) and decode
                                      requests (qo_len == 1) runs as two persistent launches side
                                      by side: the prefill kernel on part of the compute units and
-                                     the decode kernel, on a stream the plan owns, on the rest;
+                                     the decode kernel, on a side stream the plan holds (drawn
+                                     from a library-wide pool), on the rest;
                                      the caller's stream waits for both.  The split comes from
                                      the algorithmic work of each side.  (Prefill and decode
                                      co-scheduled for chunked prefill, and attention on a subset
@@ -388,8 +389,9 @@ void pka_cascade_destroy(pka_cascade* cascade);
  * completed (for example by synchronising the stream).  Its staging buffers
  * return to the library's pool with the events of their last copies (a
  * buffer is reused only once its copy has completed), so destroying a plan
- * frees no pinned memory and does not wait.  A mixed-batch plan also
- * destroys its side stream.  NULL is a no-op. */
+ * frees no pinned memory and does not wait.  A mixed-batch plan's side
+ * stream and events go back to a library-wide pool in the same way (creating
+ * a stream costs milliseconds).  NULL is a no-op. */
 void pka_plan_destroy(pka_plan* plan);
 
 #ifdef __cplusplus

@@ -107,6 +107,52 @@ void release_staging(std::vector<Staging>* held) {
   held->clear();
 }
 
+// A mixed-batch plan's side stream and its fork / join events.  Creating a
+// stream costs milliseconds, so they come from a library-wide pool (per
+// device) and go back to it when the plan is destroyed (the caller has then
+// made sure every run of the plan completed, so the stream is idle).
+struct SideStream {
+  int device = -1;
+  hipStream_t stream = nullptr;
+  hipEvent_t fork = nullptr, join = nullptr;
+};
+std::vector<SideStream> g_side_pool;  // guarded by g_pool_mu
+
+int acquire_side(SideStream* out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_error("hipGetDevice", e);
+  {
+    std::lock_guard<std::mutex> lock(g_pool_mu);
+    for (size_t i = 0; i < g_side_pool.size(); ++i)
+      if (g_side_pool[i].device == dev) {
+        *out = g_side_pool[i];
+        g_side_pool.erase(g_side_pool.begin() + static_cast<std::ptrdiff_t>(i));
+        return PKA_OK;
+      }
+  }
+  SideStream s;
+  s.device = dev;
+  // default priority, like every stream here
+  e = hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&s.fork, hipEventDisableTiming);
+  if (e == hipSuccess) e = hipEventCreateWithFlags(&s.join, hipEventDisableTiming);
+  if (e != hipSuccess) {
+    if (s.join) (void)hipEventDestroy(s.join);
+    if (s.fork) (void)hipEventDestroy(s.fork);
+    if (s.stream) (void)hipStreamDestroy(s.stream);
+    return hip_error("plan side stream", e);
+  }
+  *out = s;
+  return PKA_OK;
+}
+
+void release_side(const SideStream& s) {
+  if (!s.stream) return;
+  std::lock_guard<std::mutex> lock(g_pool_mu);
+  g_side_pool.push_back(s);
+}
+
 }  // namespace
 
 struct pka_plan {
@@ -126,10 +172,9 @@ struct pka_plan {
   std::vector<Staging> staging;
   int32_t num_parts;
   PartLaunch parts[2];
-  // PKA_MIXED_BATCH: the decode launch runs on `side`, forked from and joined
-  // back into the caller's stream with the two events.
-  hipStream_t side;
-  hipEvent_t fork, join;
+  // PKA_MIXED_BATCH: the decode launch runs on side.stream, forked from and
+  // joined back into the caller's stream with the two events.
+  SideStream side;
 };
 
 // A cascade: one plan per level over its share of the workspaces, and the
@@ -296,17 +341,17 @@ int run_common(const pka_plan* p, const void* q, const void* k, const void* v, c
   // that its workgroups take their compute units before the decode launch
   // (forked onto the plan's side stream) fills the rest; the caller's stream
   // then waits for the side stream.  The two write disjoint output rows.
-  hipError_t e = hipEventRecord(p->fork, stream);
+  hipError_t e = hipEventRecord(p->side.fork, stream);
   if (e != hipSuccess) return hip_error("hipEventRecord(fork)", e);
-  e = hipStreamWaitEvent(p->side, p->fork, 0);
+  e = hipStreamWaitEvent(p->side.stream, p->side.fork, 0);
   if (e != hipSuccess) return hip_error("hipStreamWaitEvent(fork)", e);
   int st = run_part(p, p->parts[0], q, k, v, kv, o, lse, float_base, stream);
   if (st != PKA_OK) return st;
-  st = run_part(p, p->parts[1], q, k, v, kv, o, lse, float_base, p->side);
+  st = run_part(p, p->parts[1], q, k, v, kv, o, lse, float_base, p->side.stream);
   if (st != PKA_OK) return st;
-  e = hipEventRecord(p->join, p->side);
+  e = hipEventRecord(p->side.join, p->side.stream);
   if (e != hipSuccess) return hip_error("hipEventRecord(join)", e);
-  e = hipStreamWaitEvent(stream, p->join, 0);
+  e = hipStreamWaitEvent(stream, p->side.join, 0);
   if (e != hipSuccess) return hip_error("hipStreamWaitEvent(join)", e);
   return PKA_OK;
 }
@@ -353,17 +398,11 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     p->float_ws = float_ws;
     p->int_ws_bytes = int_ws_bytes;
     p->float_ws_bytes = float_ws_bytes;
-    p->side = nullptr;
-    p->fork = p->join = nullptr;
-    hipError_t e = hipSuccess;
     if (flags & PKA_MIXED_BATCH) {
-      // default priority, like every stream here
-      e = hipStreamCreateWithFlags(&p->side, hipStreamNonBlocking);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&p->fork, hipEventDisableTiming);
-      if (e == hipSuccess) e = hipEventCreateWithFlags(&p->join, hipEventDisableTiming);
-      if (e != hipSuccess) {
+      st = acquire_side(&p->side);
+      if (st != PKA_OK) {
         pka_plan_destroy(p);
-        return hip_error("plan side stream", e);
+        return st;
       }
     }
     st = upload(p, res, batch, (flags & PKA_RAGGED_KV) ? 0 : nnz_pages, stream);
@@ -674,9 +713,7 @@ void pka_cascade_destroy(pka_cascade* c) {
 
 void pka_plan_destroy(pka_plan* plan) {
   if (!plan_ok(plan)) return;
-  if (plan->fork) (void)hipEventDestroy(plan->fork);
-  if (plan->join) (void)hipEventDestroy(plan->join);
-  if (plan->side) (void)hipStreamDestroy(plan->side);
+  release_side(plan->side);  // back to the pool, idle (the caller waited for the runs)
   release_staging(&plan->staging);  // pooled with their events, never freed here
   plan->magic = 0;
   delete plan;

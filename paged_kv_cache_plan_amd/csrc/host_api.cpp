@@ -114,7 +114,7 @@ int plan_or_error(const PlanInput& in, Planned* res) {
 }
 
 int plan_for_create(const PlanInput& in, Planned* res) {
-  if (g_cached && !(in.flags & kFlagMixed) && g_cache_key.same(in)) {
+  if (g_cached && g_cache_key.same(in)) {
     g_cached = false;
     Planned pl = std::move(g_cache_plan);
     if (!(in.flags & kFlagRagged)) {
@@ -127,6 +127,25 @@ int plan_for_create(const PlanInput& in, Planned* res) {
       std::vector<int32_t>& im = pl.mp.single.image;
       if (in.nnz_pages > 0)
         std::memcpy(im.data() + im[kHdrOffIndices], in.kv_indices, static_cast<size_t>(in.nnz_pages) * sizeof(int32_t));
+      if (pl.mp.mixed) {
+        // Each sub-image holds the page ids of its own requests (prefill:
+        // qo_len > 1, decode: qo_len == 1), request after request, at its
+        // indices section; the two sit at their offsets in the mixed image.
+        auto fill = [&](int32_t off, bool prefill_side) {
+          int32_t* sub = pl.mp.image.data() + off;
+          int32_t* dst = sub + sub[kHdrOffIndices];
+          for (int32_t r = 0; r < in.batch; ++r) {
+            const int32_t n = in.qo_indptr[r + 1] - in.qo_indptr[r];
+            if (prefill_side ? n > 1 : n == 1) {
+              const int32_t a = in.kv_indptr[r], b = in.kv_indptr[r + 1];
+              if (b > a) std::memcpy(dst, in.kv_indices + a, static_cast<size_t>(b - a) * sizeof(int32_t));
+              dst += b - a;
+            }
+          }
+        };
+        fill(pl.mp.off_prefill, true);
+        fill(pl.mp.off_decode, false);
+      }
     }
     *res = std::move(pl);
     return PKA_OK;
@@ -257,7 +276,7 @@ int pka_plan_workspace_size(const int32_t* qo_indptr, const int32_t* kv_indptr,
     if (st != PKA_OK) return st;
     *int_ws_bytes = res.image().size() * sizeof(int32_t);
     *float_ws_bytes = res.float_ws_bytes();
-    if (!(flags & PKA_MIXED_BATCH)) {
+    {
       pka::g_cache_key = pka::PlanKey::of(in);
       pka::g_cache_plan = std::move(res);
       pka::g_cached = true;
