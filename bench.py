@@ -250,11 +250,12 @@ def _sub_batch(w, rs):
 
 def bench_mixed(w, dev, steps, warmup, copies=2):
     """One chunked-prefill serving step (prefill chunks and decode requests in
-    one batch), three ways, each timed with HIP events on the caller's stream:
-    (a) PKA_MIXED_BATCH: the prefill and decode kernels side by side on a
-    split of the compute units; (b) one ordinary plan, whose prefill kernel
-    takes every row; (c) the prefill requests, then the decode requests, as
-    two plans run one after the other."""
+    one batch), four ways, each timed with HIP events on the caller's stream:
+    (a) PKA_MIXED_BATCH: one launch whose workgroups serve both kinds;
+    (b) with PKA_MIXED_TWO_LAUNCHES: the prefill and decode kernels side by
+    side on a split of the compute units; (c) one ordinary plan, whose
+    prefill kernel takes every row; (d) the prefill requests, then the decode
+    requests, as two plans run one after the other."""
     import torch
     import paged_kv_cache_plan_amd as pka
     mk = lambda qo, kv, idx, last, **kw: pka.Plan(qo, kv, idx, last, w.num_qo_heads, w.num_kv_heads, w.head_dim,
@@ -272,6 +273,7 @@ def bench_mixed(w, dev, steps, warmup, copies=2):
             plan_mixed.close()
     plan_ms_first = times[0]
     plan_ms = sorted(times[1:])[5]
+    plan_two = mk(*full, mixed_two_launches=True)
     plan_whole = mk(*full)
     pre = [r for r in range(w.batch) if w.qo_lens[r] > 1]
     dec = [r for r in range(w.batch) if w.qo_lens[r] == 1]
@@ -290,6 +292,9 @@ def bench_mixed(w, dev, steps, warmup, copies=2):
     def run_mixed(i):
         plan_mixed.run(qs[i % copies], pools[i % copies], o, lse)
 
+    def run_two(i):
+        plan_two.run(qs[i % copies], pools[i % copies], o, lse)
+
     def run_whole(i):
         plan_whole.run(qs[i % copies], pools[i % copies], o, lse)
 
@@ -299,11 +304,12 @@ def bench_mixed(w, dev, steps, warmup, copies=2):
 
     res = {"kernel": "mixed", "plan_ms": plan_ms, "plan_ms_first": plan_ms_first, "requests_prefill": len(pre), "requests_decode": len(dec),
            "prefill_cus": plan_mixed.info["prefill_cus"], "decode_cus": plan_mixed.info["decode_cus"]}
-    for name, fn in (("mixed", run_mixed), ("single_launch", run_whole), ("sequential", run_seq)):
+    for name, fn in (("mixed", run_mixed), ("two_launches", run_two), ("single_launch", run_whole),
+                     ("sequential", run_seq)):
         _, per = time_launches(fn, steps, warmup)
         res[f"{name}_ms_avg"] = sum(per) / len(per)
         res[f"{name}_ms_median"] = sorted(per)[len(per) // 2]
-    for p in (plan_mixed, plan_whole, plan_p, plan_d):
+    for p in (plan_mixed, plan_two, plan_whole, plan_p, plan_d):
         p.close()
     flop = 4.0 * D * H * visible_pairs([w.qo_lens[r] for r in pre], [w.kv_lens[r] for r in pre], w.causal)
     kv_bytes = 4.0 * w.num_kv_heads * D * sum(w.kv_lens[r] for r in dec)
@@ -311,6 +317,7 @@ def bench_mixed(w, dev, steps, warmup, copies=2):
     res.update({"prefill_flops": flop, "decode_kv_bytes": kv_bytes,
                 "speedup_vs_sequential": res["sequential_ms_avg"] / res["mixed_ms_avg"],
                 "speedup_vs_single_launch": res["single_launch_ms_avg"] / res["mixed_ms_avg"],
+                "speedup_vs_two_launches": res["two_launches_ms_avg"] / res["mixed_ms_avg"],
                 "ms_per_step": res["mixed_ms_avg"]})
     del qs, pools, q_p, q_d, o, lse
     torch.cuda.empty_cache()

@@ -82,18 +82,27 @@ enum {
                                      workspaces (FlashInfer 0.2 release blog, "CUDAGraph
                                      compatibility for variable-length inputs")              */
 #define PKA_MIXED_BATCH 0x10u     /* a batch with both prefill requests (qo_len > 1) and decode
-                                     requests (qo_len == 1) runs as two persistent launches side
-                                     by side: the prefill kernel on part of the compute units and
-                                     the decode kernel, on a side stream the plan holds (drawn
-                                     from a library-wide pool), on the rest;
-                                     the caller's stream waits for both.  The split comes from
-                                     the algorithmic work of each side.  (Prefill and decode
-                                     co-scheduled for chunked prefill, and attention on a subset
-                                     of the compute units: "[Roadmap] FlashInfer v0.2 to v0.3",
-                                     milestones "POD-Attention Integration" and "Nanoflow
-                                     Parallelism"; FlashInfer documentation contents,
-                                     "flashinfer.pod".)  A batch of one kind plans as without the
-                                     flag.  Not with PKA_GRAPH_STABLE; not for pka_debug_gather. */
+                                     requests (qo_len == 1) runs as one persistent launch whose
+                                     workgroups serve both kinds, one after the other: those of
+                                     the compute units that a cost model (the algorithmic work
+                                     of each side) gives decode start with decode units, the
+                                     others with prefill units, and whichever kind runs out
+                                     first, its workgroups move on to the other.  (Prefill and
+                                     decode in one kernel for chunked prefill: "[Roadmap]
+                                     FlashInfer v0.2 to v0.3", milestone "POD-Attention
+                                     Integration"; FlashInfer documentation contents,
+                                     "flashinfer.pod".)  A batch of one kind plans as without
+                                     the flag.  Not with PKA_GRAPH_STABLE; not for
+                                     pka_debug_gather.                                          */
+#define PKA_MIXED_TWO_LAUNCHES 0x20u /* with PKA_MIXED_BATCH: two persistent launches side by side
+                                     instead of one: the prefill kernel on the compute units
+                                     the cost model gives prefill and the decode kernel, on a
+                                     side stream the plan holds (drawn from a library-wide
+                                     pool), on the rest; the caller's stream waits for both
+                                     (attention on a subset of the compute units: "[Roadmap]
+                                     FlashInfer v0.2 to v0.3", milestone "Nanoflow
+                                     Parallelism").  Without PKA_MIXED_BATCH it is an invalid
+                                     argument.                                                 */
 
 /* Which attention kernel a plan launches. */
 enum { PKA_KERNEL_PREFILL = 0, PKA_KERNEL_DECODE = 1, PKA_KERNEL_MIXED = 2 };
@@ -113,10 +122,13 @@ typedef struct pka_plan_info {
   int64_t int_ws_bytes;     /* bytes of the int workspace image the plan uploads            */
   int64_t float_ws_bytes;   /* bytes of float workspace the runs need                       */
   int32_t num_workers;      /* workgroups of the persistent attention launch (prefill: each
-                               takes units from its XCD's queue, then from the others)     */
+                               takes units from its XCD's queue, then from the others; a
+                               mixed batch in one launch: the workgroups serving both kinds) */
   int32_t num_queues;       /* unit queues: one per XCD for prefill, one for decode          */
-  int32_t prefill_cus;      /* mixed batch: compute units the prefill launch is sized for    */
-  int32_t decode_cus;       /* mixed batch: compute units the decode launch is sized for     */
+  int32_t prefill_cus;      /* mixed batch: compute units whose workgroups start with prefill
+                               units (two launches: the prefill launch's compute units)      */
+  int32_t decode_cus;       /* mixed batch: compute units whose workgroups start with decode
+                               units (two launches: the decode launch's compute units)       */
 } pka_plan_info;
 
 /* Message for the last failed call on this thread ("" if none). */
@@ -389,9 +401,9 @@ void pka_cascade_destroy(pka_cascade* cascade);
  * completed (for example by synchronising the stream).  Its staging buffers
  * return to the library's pool with the events of their last copies (a
  * buffer is reused only once its copy has completed), so destroying a plan
- * frees no pinned memory and does not wait.  A mixed-batch plan's side
- * stream and events go back to a library-wide pool in the same way (creating
- * a stream costs milliseconds).  NULL is a no-op. */
+ * frees no pinned memory and does not wait.  The side stream and events of a
+ * PKA_MIXED_TWO_LAUNCHES plan go back to a library-wide pool in the same way
+ * (creating a stream costs milliseconds).  NULL is a no-op. */
 void pka_plan_destroy(pka_plan* plan);
 
 #ifdef __cplusplus

@@ -31,6 +31,7 @@ PKA_OUT_FP32 = 0x2
 PKA_RAGGED_KV = 0x4
 PKA_GRAPH_STABLE = 0x8
 PKA_MIXED_BATCH = 0x10
+PKA_MIXED_TWO_LAUNCHES = 0x20
 
 PKA_KERNEL_PREFILL = 0
 PKA_KERNEL_DECODE = 1
@@ -243,21 +244,24 @@ class Plan:
     after ``update``; size their workspaces for the largest batch with
     ``int_ws_bytes`` / ``float_ws_bytes`` (at least what this batch needs is
     allocated).  ``mixed`` plans a batch of prefill and decode requests as
-    two concurrent launches over a split of the compute units.
+    one launch whose workgroups serve both kinds, one after the other;
+    ``mixed_two_launches`` as two concurrent launches over a split of the
+    compute units.
     """
 
     def __init__(self, qo_indptr, kv_indptr, kv_indices, kv_last_page_len, num_qo_heads,
                  num_kv_heads, head_dim, page_size=1, causal=True, sm_scale=None,
                  num_pages=None, ragged=False, disable_split_kv=False, out_fp32=False,
                  device=None, stream=None, graph_stable=False, int_ws_bytes=0, float_ws_bytes=0,
-                 mixed=False):
+                 mixed=False, mixed_two_launches=False):
         import torch
         L = load_library()
         self._lib = L
         self._handle = ctypes.c_void_p()
         flags = (PKA_RAGGED_KV if ragged else 0) | (PKA_DISABLE_SPLIT_KV if disable_split_kv else 0) \
             | (PKA_OUT_FP32 if out_fp32 else 0) | (PKA_GRAPH_STABLE if graph_stable else 0) \
-            | (PKA_MIXED_BATCH if mixed else 0)
+            | (PKA_MIXED_BATCH if (mixed or mixed_two_launches) else 0) \
+            | (PKA_MIXED_TWO_LAUNCHES if mixed_two_launches else 0)
         self.flags = flags
         self.num_qo_heads, self.num_kv_heads, self.head_dim = num_qo_heads, num_kv_heads, head_dim
         self.page_size = page_size

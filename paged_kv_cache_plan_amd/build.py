@@ -28,7 +28,7 @@ BUILD_DIR = os.path.join(HERE, "_build")
 LIB_PATH = os.path.join(HERE, "libpka.so")
 HOST_LIB_PATH = os.path.join(HERE, "libpka_planner_host.so")
 ARCH = "gfx950"
-KERNELS = ["prefill.hip", "decode.hip", "merge.hip", "append.hip", "scratch.hip"]
+KERNELS = ["prefill.hip", "decode.hip", "mixed.hip", "merge.hip", "append.hip", "scratch.hip"]
 HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-Wno-unused-command-line-argument"]
@@ -38,7 +38,11 @@ HIP_FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}",
 KERNEL_FLAGS = {"decode.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"],
                 # the ILP-first machine scheduler: measured 1-2% faster on the
                 # short causal units of a ragged prefill batch, equal elsewhere
-                "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"]}
+                "prefill.hip": ["-mllvm", "-amdgpu-sched-strategy=max-ilp"],
+                # the one-grid mixed kernel holds both workers: the decode
+                # worker's atomic as above, and the default scheduler (with
+                # the ILP-first one its 8-wave decode part spilled)
+                "mixed.hip": ["-mllvm", "-amdgpu-atomic-optimizer-strategy=None"]}
 
 
 def _hipcc() -> str:

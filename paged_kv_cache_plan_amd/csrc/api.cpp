@@ -172,8 +172,10 @@ struct pka_plan {
   std::vector<Staging> staging;
   int32_t num_parts;
   PartLaunch parts[2];
-  // PKA_MIXED_BATCH: the decode launch runs on side.stream, forked from and
-  // joined back into the caller's stream with the two events.
+  bool one_grid;  // a mixed batch in one launch (not PKA_MIXED_TWO_LAUNCHES)
+  int32_t xcds, decode_first_slots;  // one grid: which workgroups start with decode
+  // PKA_MIXED_TWO_LAUNCHES: the decode launch runs on side.stream, forked
+  // from and joined back into the caller's stream with the two events.
   SideStream side;
 };
 
@@ -240,6 +242,9 @@ int upload(pka_plan* p, const Planned& pl, int32_t batch, int32_t nnz, hipStream
   p->off_merge = res.image[pka::kHdrOffMerge];
   p->off_idx = res.image[pka::kHdrOffIndices];
   p->off_sched = res.image[pka::kHdrOffSched];
+  p->one_grid = pl.mp.mixed && pl.mp.one_grid;
+  p->xcds = pl.mp.xcds;
+  p->decode_first_slots = pl.mp.decode_first_slots;
   if (pl.mp.mixed) {
     const pka::MixedPlan& mp = pl.mp;
     p->num_parts = 2;
@@ -295,18 +300,10 @@ pka::AttnArgs attn_args(const pka_plan* p, const PartLaunch& part, const void* q
   return a;
 }
 
-// One part's attention launch and, if it split any KV, its merge.
-int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const void* k, const void* v,
-             const KvLayout& kv, void* o, float* lse, void* float_base, hipStream_t stream) {
+// A part's split merge, if it split any KV (a graph-stable plan: always).
+int run_merge(const pka_plan* p, const PartLaunch& part, const pka::AttnArgs& a, void* o, float* lse,
+              hipStream_t stream) {
   const bool stable = (p->flags & PKA_GRAPH_STABLE) != 0;
-  const pka::AttnArgs a = attn_args(p, part, q, k, v, kv, o, lse, float_base);
-  const bool paged = !(p->flags & PKA_RAGGED_KV);
-  hipError_t e;
-  if (part.kernel == PKA_KERNEL_DECODE)
-    e = pka::launch_decode(a, p->head_dim, paged, part.num_workers, stream);
-  else
-    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, part.num_workers, stream);
-  if (e != hipSuccess) return hip_error("attention launch", e);
   if (part.num_merge > 0 || stable) {
     pka::MergeArgs m{};
     m.part_o = a.part_o;
@@ -319,10 +316,24 @@ int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const voi
     // one workgroup per (slice, group), up to a cap (the kernel is grid-stride)
     const int64_t pairs = int64_t(part.num_merge) * std::max(1, part.merge_slices);
     const int grid = stable ? pka::kMergeGrid : static_cast<int>(std::min<int64_t>(pairs, 8 * pka::kMergeGrid));
-    e = pka::launch_merge(m, p->head_dim, grid, stream);
+    const hipError_t e = pka::launch_merge(m, p->head_dim, grid, stream);
     if (e != hipSuccess) return hip_error("merge launch", e);
   }
   return PKA_OK;
+}
+
+// One part's attention launch and, if it split any KV, its merge.
+int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const void* k, const void* v,
+             const KvLayout& kv, void* o, float* lse, void* float_base, hipStream_t stream) {
+  const pka::AttnArgs a = attn_args(p, part, q, k, v, kv, o, lse, float_base);
+  const bool paged = !(p->flags & PKA_RAGGED_KV);
+  hipError_t e;
+  if (part.kernel == PKA_KERNEL_DECODE)
+    e = pka::launch_decode(a, p->head_dim, paged, part.num_workers, stream);
+  else
+    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, part.num_workers, stream);
+  if (e != hipSuccess) return hip_error("attention launch", e);
+  return run_merge(p, part, a, o, lse, stream);
 }
 
 // float_base: where the plan's partial states go (its float workspace, or
@@ -337,6 +348,19 @@ int run_common(const pka_plan* p, const void* q, const void* k, const void* v, c
   if (!q || !o) return set_error(PKA_ERR_INVALID_ARG, "q and o must not be NULL");
   if (p->info.total_kv > 0 && !k) return set_error(PKA_ERR_INVALID_ARG, "KV pointer must not be NULL");
   if (p->num_parts == 1) return run_part(p, p->parts[0], q, k, v, kv, o, lse, float_base, stream);
+  if (p->one_grid) {
+    // One launch serves both images (the planner gave both the same worker
+    // count), then each part's merge.
+    const pka::AttnArgs ap = attn_args(p, p->parts[0], q, k, v, kv, o, lse, float_base);
+    const pka::AttnArgs ad = attn_args(p, p->parts[1], q, k, v, kv, o, lse, float_base);
+    const pka::MixedGrid g{p->parts[0].num_workers, p->xcds, p->decode_first_slots};
+    const hipError_t e =
+        pka::launch_mixed(ap, ad, p->head_dim, !(p->flags & PKA_RAGGED_KV), p->causal != 0, g, stream);
+    if (e != hipSuccess) return hip_error("mixed attention launch", e);
+    const int st = run_merge(p, p->parts[0], ap, o, lse, stream);
+    if (st != PKA_OK) return st;
+    return run_merge(p, p->parts[1], ad, o, lse, stream);
+  }
   // Mixed batch: the prefill launch goes first, on the caller's stream, so
   // that its workgroups take their compute units before the decode launch
   // (forked onto the plan's side stream) fills the rest; the caller's stream
@@ -398,7 +422,7 @@ int pka_plan_create(const int32_t* qo_indptr, const int32_t* kv_indptr, const in
     p->float_ws = float_ws;
     p->int_ws_bytes = int_ws_bytes;
     p->float_ws_bytes = float_ws_bytes;
-    if (flags & PKA_MIXED_BATCH) {
+    if ((flags & PKA_MIXED_BATCH) && (flags & PKA_MIXED_TWO_LAUNCHES)) {
       st = acquire_side(&p->side);
       if (st != PKA_OK) {
         pka_plan_destroy(p);

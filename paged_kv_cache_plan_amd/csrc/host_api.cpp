@@ -168,7 +168,8 @@ void fill_plan_info(const Planned& pl, int32_t batch, int32_t nnz, pka_plan_info
   info->kv_chunk = b.kv_chunk;
   info->int_ws_bytes = static_cast<int64_t>(mp.image.size() * sizeof(int32_t));
   info->float_ws_bytes = static_cast<int64_t>(mp.float_ws_bytes);
-  info->num_workers = a.num_workers + b.num_workers;
+  // one grid: the same workgroups serve both images
+  info->num_workers = mp.one_grid ? a.num_workers : a.num_workers + b.num_workers;
   info->num_queues = a.num_queues + b.num_queues;
   info->prefill_cus = mp.prefill_cus;
   info->decode_cus = mp.decode_cus;

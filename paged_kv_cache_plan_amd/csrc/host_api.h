@@ -13,7 +13,7 @@
 namespace pka {
 
 constexpr uint32_t kKnownFlags =
-    PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV | PKA_GRAPH_STABLE | PKA_MIXED_BATCH;
+    PKA_DISABLE_SPLIT_KV | PKA_OUT_FP32 | PKA_RAGGED_KV | PKA_GRAPH_STABLE | PKA_MIXED_BATCH | PKA_MIXED_TWO_LAUNCHES;
 
 // Record msg as this thread's last error and return code.
 int set_error(int code, const std::string& msg);

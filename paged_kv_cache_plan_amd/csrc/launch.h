@@ -10,6 +10,14 @@ namespace pka {
 hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool paged, bool causal, int grid,
                           hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, int head_dim, bool paged, int grid, hipStream_t stream);
+// One-grid mixed batch: every workgroup runs the prefill worker and the decode
+// worker (the two images' worker counts both equal grid); workgroup b starts
+// with decode when b / xcds < decode_first_slots.
+struct MixedGrid {
+  int grid, xcds, decode_first_slots;
+};
+hipError_t launch_mixed(const AttnArgs& prefill, const AttnArgs& decode, int head_dim, bool paged, bool causal,
+                        const MixedGrid& g, hipStream_t stream);
 hipError_t launch_merge(const MergeArgs& a, int head_dim, int grid, hipStream_t stream);
 hipError_t launch_merge_states(const MergeStatesArgs& a, hipStream_t stream);
 hipError_t launch_gather(const GatherArgs& a, int batch, hipStream_t stream);

@@ -288,11 +288,13 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   const int32_t n_queues = static_cast<int32_t>(queue_begin.size()) - 1;
   int64_t longest = 0;
   for (int q = 0; q < n_queues; ++q) longest = std::max<int64_t>(longest, queue_begin[q + 1] - queue_begin[q]);
-  const int64_t slots =
-      int64_t(std::max(1, in.num_cus)) * (decode ? kDecodeWgPerCu : prefill_wg_per_cu(in.head_dim));
+  const int64_t slots = in.workers_override > 0
+                            ? int64_t(in.workers_override)
+                            : int64_t(std::max(1, in.num_cus)) * (decode ? kDecodeWgPerCu : prefill_wg_per_cu(in.head_dim));
   const int64_t per_queue_max = std::max<int64_t>(1, slots / n_queues);
-  const int32_t workers_per_queue =
-      static_cast<int32_t>(fixed ? per_queue_max : std::max<int64_t>(1, std::min<int64_t>(longest, per_queue_max)));
+  const int32_t workers_per_queue = static_cast<int32_t>(
+      (fixed || in.workers_override > 0) ? per_queue_max
+                                         : std::max<int64_t>(1, std::min<int64_t>(longest, per_queue_max)));
   const int32_t n_workers = n_queues * workers_per_queue;
 
   // Assemble the image.
@@ -389,7 +391,9 @@ int build_mixed_plan(const PlanInput& in, MixedPlan* out, std::string* err) {
   // The whole batch is always planned first: it validates every array, with
   // the batch's own request numbers in the messages.
   PlanInput whole = in;
-  whole.flags &= ~kFlagMixed;
+  whole.flags &= ~(kFlagMixed | kFlagMixedTwoLaunches);
+  if ((in.flags & kFlagMixedTwoLaunches) && !(in.flags & kFlagMixed))
+    return fail(err, kInvalid, "the two-launch flag needs the mixed-batch flag");
   int st = build_plan(whole, &out->single, err);
   if (st != kOk || !(in.flags & kFlagMixed)) return st;
   if (in.flags & kFlagGraphStable)
@@ -455,16 +459,36 @@ int build_mixed_plan(const PlanInput& in, MixedPlan* out, std::string* err) {
   int32_t pcus = in.prefill_cus_override > 0 ? in.prefill_cus_override
                                              : mixed_prefill_cus(flop, bytes, in.num_cus, in.num_xcds);
   pcus = std::max(1, std::min(pcus, in.num_cus - 1));
-  ip.num_cus = pcus;
-  id.num_cus = in.num_cus - pcus;
-
-  st = build_plan(ip, &out->prefill, err);
-  if (st != kOk) return st;
-  st = build_plan(id, &out->decode, err);
-  if (st != kOk) return st;
+  if (!(in.flags & kFlagMixedTwoLaunches)) {
+    // One launch: both sides planned for the whole chip; the decode side
+    // gets exactly as many workers as the prefill side ended with (its one
+    // queue then has every workgroup of the launch).
+    ip.num_cus = id.num_cus = in.num_cus;
+    ip.workers_override = std::max(1, in.num_cus) * prefill_wg_per_cu(in.head_dim);
+    st = build_plan(ip, &out->prefill, err);
+    if (st != kOk) return st;
+    id.workers_override = out->prefill.num_workers;
+    st = build_plan(id, &out->decode, err);
+    if (st != kOk) return st;
+    if (out->decode.num_workers != out->prefill.num_workers)
+      return fail(err, kUnsupported, "one-grid mixed plan: worker counts differ");
+    out->one_grid = true;
+    // the cost model's split decides which workgroups start with decode
+    out->prefill_cus = pcus;
+    out->decode_cus = in.num_cus - pcus;
+    out->xcds = std::max(1, in.num_xcds);
+    out->decode_first_slots = (in.num_cus - pcus) / out->xcds * prefill_wg_per_cu(in.head_dim);
+  } else {
+    ip.num_cus = pcus;
+    id.num_cus = in.num_cus - pcus;
+    st = build_plan(ip, &out->prefill, err);
+    if (st != kOk) return st;
+    st = build_plan(id, &out->decode, err);
+    if (st != kOk) return st;
+    out->prefill_cus = pcus;
+    out->decode_cus = in.num_cus - pcus;
+  }
   out->mixed = true;
-  out->prefill_cus = pcus;
-  out->decode_cus = in.num_cus - pcus;
   out->off_prefill = kMixWords;
   out->off_decode = out->off_prefill + align_words(static_cast<int64_t>(out->prefill.image.size()));
   out->float_off_decode = (out->prefill.float_ws_bytes + 255) / 256 * 256;
@@ -480,6 +504,8 @@ int build_mixed_plan(const PlanInput& in, MixedPlan* out, std::string* err) {
   im[kMixDecodeCus] = out->decode_cus;
   im[kMixBatch] = B;
   im[kMixNnz] = ragged ? 0 : in.kv_indptr[B];
+  im[kMixOneGrid] = out->one_grid ? 1 : 0;
+  im[kMixDecodeFirstSlots] = out->decode_first_slots;
   std::memcpy(im + out->off_prefill, out->prefill.image.data(), out->prefill.image.size() * sizeof(int32_t));
   std::memcpy(im + out->off_decode, out->decode.image.data(), out->decode.image.size() * sizeof(int32_t));
   return kOk;

@@ -135,7 +135,8 @@ constexpr uint32_t kFlagDisableSplit = 0x1u;
 constexpr uint32_t kFlagOutFp32 = 0x2u;
 constexpr uint32_t kFlagRagged = 0x4u;
 constexpr uint32_t kFlagGraphStable = 0x8u;  // launch shapes that do not depend on the batch
-constexpr uint32_t kFlagMixed = 0x10u;       // prefill and decode requests as two concurrent launches
+constexpr uint32_t kFlagMixed = 0x10u;       // prefill and decode requests together, in one launch
+constexpr uint32_t kFlagMixedTwoLaunches = 0x20u;  // with kFlagMixed: two launches on a compute-unit split
 
 enum Status : int { kOk = 0, kInvalid = 1, kUnsupported = 2, kWorkspace = 3, kHip = 4 };
 
@@ -163,6 +164,9 @@ struct PlanInput {
   const int32_t* qo_begin = nullptr;
   const int32_t* kv_begin = nullptr;
   int32_t prefill_cus_override = 0;  // >0: compute units of a mixed plan's prefill launch (tuning)
+  // >0: exactly this many workers, the same number for every queue (a
+  // launch whose workgroups also serve another plan's queues)
+  int32_t workers_override = 0;
 };
 
 // Prefill workgroup shape per head_dim: 32 packed query rows per wave, 8
@@ -198,12 +202,18 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err);
 int check_page_ids(const int32_t* kv_indices, int32_t nnz, int32_t num_pages, std::string* err);
 
 // A mixed batch (kFlagMixed with both prefill requests, qo_len > 1, and
-// decode requests, qo_len == 1) runs as two persistent launches side by
-// side: the prefill kernel on part of the compute units and the decode
-// kernel on the rest, each planned over its own requests as an ordinary
-// image.  The int workspace holds a 64-word header, then the prefill image,
-// then the decode image; the float workspace holds the prefill partial
-// states, then the decode ones.
+// decode requests, qo_len == 1) is planned as two images, each over its own
+// requests as an ordinary batch.  By default both run in one persistent
+// launch: the images are planned for the whole chip and the same number of
+// workers, and every workgroup serves both, one kind after the other.  The
+// workgroups of decode_cus compute units (from the cost model below) start
+// with the decode queue, the others with the prefill queues; a workgroup
+// whose first kind runs out of units moves on to the other kind's queues,
+// so the split adjusts itself to the speeds met.  With kFlagMixedTwoLaunches
+// they run as two persistent launches side by side instead: the prefill
+// kernel on prefill_cus compute units and the decode kernel on the rest.  The int workspace holds a 64-word header, then the
+// prefill image, then the decode image; the float workspace holds the
+// prefill partial states, then the decode ones.
 enum MixedField : int {
   kMixMagic = 0,
   kMixKernel,          // kMixed
@@ -214,6 +224,8 @@ enum MixedField : int {
   kMixDecodeCus,
   kMixBatch,
   kMixNnz,
+  kMixOneGrid,  // 1: one launch serves both images (its workgroup count: each image's workers)
+  kMixDecodeFirstSlots,  // one grid: workgroup slots per XCD that start with the decode queue
   kMixWords = 64
 };
 constexpr int32_t kMixedMagic = 0x4d414b50;  // "PKAM"
@@ -231,6 +243,9 @@ struct MixedPlan {
   PlanResult single;       // the plan of the whole batch (always built: it validates)
   PlanResult prefill, decode;
   int32_t prefill_cus = 0, decode_cus = 0;
+  bool one_grid = false;  // one launch (not kFlagMixedTwoLaunches): prefill.num_workers == decode.num_workers
+  // one grid: workgroup b starts with the decode queue when b / xcds < decode_first_slots
+  int32_t xcds = 0, decode_first_slots = 0;
   int32_t off_prefill = 0, off_decode = 0;  // words
   size_t float_off_decode = 0;              // bytes
   std::vector<int32_t> image;               // mixed: header + both images

@@ -1,15 +1,23 @@
-"""GPU parity of mixed prefill + decode batches (PKA_MIXED_BATCH): the
-prefill launch and the decode launch run side by side on a split of the
-compute units and write disjoint output rows.
+"""GPU parity of mixed prefill + decode batches (PKA_MIXED_BATCH).
 
+By default a mixed batch runs as one launch whose workgroups serve both
+kinds (the decode worker with the prefill workgroup's waves, 8 at D=128):
 * every row against the CPU oracle (tolerance);
+* without split KV, its prefill rows bit-identical to the prefill kernel
+  (the same worker code), and at D=64, where the wave counts agree, its
+  decode rows to the decode kernel;
+* repeated runs bit for bit (the queues' counters reset after every run),
+  fp32 output, ragged K/V, and the full-size chunked-prefill serving step
+  on sampled prefill rows and every decode row.
+
+With PKA_MIXED_TWO_LAUNCHES the prefill launch and the decode launch run side
+by side on a split of the compute units and write disjoint output rows:
+* every row against the CPU oracle;
 * without split KV, bit-identical to each kernel run on its own: the prefill
   rows to an ordinary plan of the whole batch (whose prefill kernel takes
   every row), the decode rows to a plan of the decode requests alone;
-* the full-size chunked-prefill serving step on sampled prefill rows and
-  every decode row;
-* ragged K/V, fp32 output, and repeated runs (the plan's side stream and
-  events are reused) bit for bit."""
+* the full-size serving step, ragged K/V, fp32 output, and repeated runs
+  (the plan's side stream and events are reused) bit for bit."""
 import random
 import time
 
@@ -77,13 +85,13 @@ def _bits(x):
 
 
 @pytest.mark.parametrize("seed,D,ps", [(0, 128, 16), (1, 128, 1), (2, 64, 4), (3, 128, 3)])
-def test_mixed_matches_oracle_and_each_kernel(seed, D, ps):
+def test_two_launches_match_oracle_and_each_kernel(seed, D, ps):
     w = _mixed(seed, D, ps)
-    o, lse, info = _run(w, mixed=True)
+    o, lse, info = _run(w, mixed_two_launches=True)
     assert info["kernel"] == pka.PKA_KERNEL_MIXED
     compare(o.float(), lse, *oracle_paged(w), f"mixed seed {seed}")
     # no split: each kernel's rows equal that kernel run on its own
-    o1, l1, info1 = _run(w, mixed=True, disable_split_kv=True)
+    o1, l1, info1 = _run(w, mixed_two_launches=True, disable_split_kv=True)
     assert info1["kernel"] == pka.PKA_KERNEL_MIXED and info1["num_merge_groups"] == 0
     op, lp, infop = _run(w, disable_split_kv=True)
     assert infop["kernel"] == pka.PKA_KERNEL_PREFILL
@@ -94,9 +102,9 @@ def test_mixed_matches_oracle_and_each_kernel(seed, D, ps):
     assert torch.equal(_bits(o1[rows]), _bits(od)) and torch.equal(_bits(l1[rows]), _bits(ld))
 
 
-def test_mixed_repeat_and_fp32():
+def test_two_launches_repeat_and_fp32():
     w = _mixed(4)
-    plan = _plan(w, mixed=True, out_fp32=True)
+    plan = _plan(w, mixed_two_launches=True, out_fp32=True)
     q, pool = w.q.to(cuda()), w.paged_kv.to(cuda())
     outs = []
     for _ in range(3):
@@ -110,10 +118,10 @@ def test_mixed_repeat_and_fp32():
     compare(outs[0][0], outs[0][1], *oracle_paged(w), "mixed fp32")
 
 
-def test_mixed_ragged():
+def test_two_launches_ragged():
     w = _mixed(5, ps=1, ragged=True)
     plan = pka.Plan(w.qo_indptr, w.kv_token_indptr, None, None, w.num_qo_heads, w.num_kv_heads, w.head_dim, 1,
-                    causal=w.causal, sm_scale=w.sm_scale, ragged=True, device=cuda(), mixed=True)
+                    causal=w.causal, sm_scale=w.sm_scale, ragged=True, device=cuda(), mixed_two_launches=True)
     assert plan.info["kernel"] == pka.PKA_KERNEL_MIXED
     o, lse = plan.run_ragged(w.q.to(cuda()), w.k.to(cuda()), w.v.to(cuda()))
     torch.cuda.synchronize()
@@ -121,13 +129,13 @@ def test_mixed_ragged():
     compare(o.float().cpu(), lse.cpu(), *oracle_paged(w), "mixed ragged")
 
 
-def test_mixed_full_size():
-    """The chunked-prefill serving step as the benchmark runs it: 4 prefill
-    chunks (prefix 1024..8192, chunk 512..2048) and 192 decode requests;
-    sampled prefill rows (with every request's first and last row) and every
-    decode row against the oracle."""
+def test_two_launches_full_size():
+    """The chunked-prefill serving step the benchmark runs (4 prefill chunks,
+    prefix 1024..8192, chunk 512..2048, and 192 decode requests) as two
+    launches: sampled prefill rows (with every request's first and last row)
+    and every decode row against the oracle."""
     w = W.mixed_batch(device=cuda())
-    plan = _plan(w, mixed=True)
+    plan = _plan(w, mixed_two_launches=True)
     info = plan.info
     assert info["kernel"] == pka.PKA_KERNEL_MIXED
     assert info["prefill_cus"] + info["decode_cus"] == 256
@@ -146,3 +154,70 @@ def test_mixed_full_size():
     idx = torch.as_tensor(rows)
     err = compare(o[idx], lse[idx], ref_o, ref_l, "mixed_batch")
     print(f"mixed_batch: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
+
+
+@pytest.mark.parametrize("seed,D,ps", [(0, 128, 16), (1, 128, 1), (2, 64, 4), (3, 128, 3), (6, 64, 16)])
+def test_one_grid_matches_oracle_and_kernels(seed, D, ps):
+    w = _mixed(seed, D, ps)
+    print(f"one grid: seed {seed} D {D} ps {ps} batch {w.batch}", flush=True)
+    o, lse, info = _run(w, mixed=True)
+    assert info["kernel"] == pka.PKA_KERNEL_MIXED and info["decode_cus"] + info["prefill_cus"] == 256
+    compare(o.float(), lse, *oracle_paged(w), f"one grid seed {seed}")
+    o1, l1, info1 = _run(w, mixed=True, disable_split_kv=True)
+    assert info1["num_merge_groups"] == 0
+    op, lp, _ = _run(w, disable_split_kv=True)
+    pre = [row for r in range(w.batch) if w.qo_lens[r] > 1
+           for row in range(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1]))]
+    assert torch.equal(_bits(o1[pre]), _bits(op[pre])) and torch.equal(_bits(l1[pre]), _bits(lp[pre]))
+    if D == 64:
+        rows, od, ld = _decode_alone(w, disable_split_kv=True)
+        assert torch.equal(_bits(o1[rows]), _bits(od)) and torch.equal(_bits(l1[rows]), _bits(ld))
+
+
+def test_one_grid_repeat_and_fp32():
+    """Repeated runs of one plan are bit-identical: the last workgroup of each
+    worker resets its queue counters for the next run."""
+    w = _mixed(7)
+    plan = _plan(w, mixed=True, out_fp32=True)
+    q, pool = w.q.to(cuda()), w.paged_kv.to(cuda())
+    outs = []
+    for _ in range(4):
+        o, lse = plan.run(q, pool)
+        torch.cuda.synchronize()
+        outs.append((o.cpu(), lse.cpu()))
+    plan.close()
+    for o, lse in outs[1:]:
+        assert torch.equal(_bits(o), _bits(outs[0][0])) and torch.equal(_bits(lse), _bits(outs[0][1]))
+    compare(outs[0][0], outs[0][1], *oracle_paged(w), "one grid fp32")
+
+
+def test_one_grid_ragged():
+    w = _mixed(8, ps=1, ragged=True)
+    plan = pka.Plan(w.qo_indptr, w.kv_token_indptr, None, None, w.num_qo_heads, w.num_kv_heads, w.head_dim, 1,
+                    causal=w.causal, sm_scale=w.sm_scale, ragged=True, device=cuda(), mixed=True)
+    assert plan.info["kernel"] == pka.PKA_KERNEL_MIXED
+    o, lse = plan.run_ragged(w.q.to(cuda()), w.k.to(cuda()), w.v.to(cuda()))
+    torch.cuda.synchronize()
+    plan.close()
+    compare(o.float().cpu(), lse.cpu(), *oracle_paged(w), "one grid ragged")
+
+
+def test_one_grid_full_size():
+    """The chunked-prefill serving step as the benchmark runs it, in one
+    launch: sampled prefill rows (with every request's first and last row)
+    and every decode row against the oracle."""
+    w = W.mixed_batch(device=cuda())
+    plan = _plan(w, mixed=True)
+    assert plan.info["kernel"] == pka.PKA_KERNEL_MIXED
+    o, lse = plan.run(w.q, w.paged_kv)
+    torch.cuda.synchronize()
+    plan.close()
+    o, lse = o.float().cpu(), lse.cpu()
+    dec = [int(w.qo_indptr[r]) for r in range(w.batch) if w.qo_lens[r] == 1]
+    ends = [x for r in range(w.batch) if w.qo_lens[r] > 1 for x in (int(w.qo_indptr[r]), int(w.qo_indptr[r + 1]) - 1)]
+    rows = sample_rows(w.total_q, 512, 37, must=dec + ends)
+    wc = W.Workload(**{**w.__dict__, "q": w.q.cpu(), "paged_kv": w.paged_kv.cpu()})
+    ref_o, ref_l = oracle_paged(wc, rows=rows)
+    idx = torch.as_tensor(rows)
+    err = compare(o[idx], lse[idx], ref_o, ref_l, "one grid mixed_batch")
+    print(f"one grid mixed_batch: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)

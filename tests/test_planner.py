@@ -55,7 +55,7 @@ def _cdiv(a, b):
 
 
 def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, flags, ragged=False, D=128,
-                 num_cus=NUM_CUS, qo_begin=None, kv_begin=None):
+                 num_cus=NUM_CUS, qo_begin=None, kv_begin=None, workers=0):
     B = len(qo_indptr) - 1
     G = Hq // Hkv
     qo_len = [qo_indptr[r + 1] - qo_indptr[r] for r in range(B)]
@@ -150,8 +150,9 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
             bounds.append(len(order))
     nq = len(bounds) - 1
     longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
-    slots = num_cus * (2 if decode else wg_per_cu(D))
-    per_queue = max(1, slots // nq) if fixed else max(1, min(longest, max(1, slots // nq)))
+    # workers > 0: exactly that many, evenly over the queues (a one-grid mixed launch)
+    slots = workers if workers > 0 else num_cus * (2 if decode else wg_per_cu(D))
+    per_queue = max(1, slots // nq) if (fixed or workers > 0) else max(1, min(longest, max(1, slots // nq)))
     workers = nq * per_queue
     align = lambda w: _cdiv(w, 64) * 64
     nnz = 0 if ragged else kv_indptr[B]
@@ -211,7 +212,8 @@ def restate_mixed(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, f
     qo_len = [qo_indptr[r + 1] - qo_indptr[r] for r in range(B)]
     pre = [r for r in range(B) if qo_len[r] > 1]
     dec = [r for r in range(B) if qo_len[r] == 1]
-    plain = flags & ~pka.PKA_MIXED_BATCH
+    plain = flags & ~(pka.PKA_MIXED_BATCH | pka.PKA_MIXED_TWO_LAUNCHES)
+    one_grid = not (flags & pka.PKA_MIXED_TWO_LAUNCHES)
     if not pre or not dec or Hq // Hkv > DECODE_MAX_G:
         return restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, plain, ragged, D)
 
@@ -219,11 +221,7 @@ def restate_mixed(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, f
         span = kv_indptr[r + 1] - kv_indptr[r]
         return span if ragged else (0 if span == 0 else (span - 1) * ps + last[r])
 
-    flop = sum(4.0 * D * Hq * bench.visible_pairs([qo_len[r]], [kv_len(r)], causal) for r in pre)
-    nbytes = sum(4.0 * Hkv * D * kv_len(r) for r in dec)
-    pcus = restate_mixed_cus(flop, nbytes)
-
-    def sub(rs, cus):
+    def sub(rs, cus, workers=0):
         qi, ki, idx = [0], [0], []
         for r in rs:
             qi.append(qi[-1] + qo_len[r])
@@ -232,15 +230,28 @@ def restate_mixed(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, f
                 idx += kv_indices[kv_indptr[r]:kv_indptr[r + 1]]
         return restate_plan(qi, ki, idx, None if ragged else [last[r] for r in rs], Hq, Hkv, ps, causal, plain,
                             ragged, D, num_cus=cus, qo_begin=[qo_indptr[r] for r in rs],
-                            kv_begin=[kv_indptr[r] for r in rs])
+                            kv_begin=[kv_indptr[r] for r in rs], workers=workers)
 
-    ip, idc = sub(pre, pcus), sub(dec, NUM_CUS - pcus)
+    flop = sum(4.0 * D * Hq * bench.visible_pairs([qo_len[r]], [kv_len(r)], causal) for r in pre)
+    nbytes = sum(4.0 * Hkv * D * kv_len(r) for r in dec)
+    pcus = restate_mixed_cus(flop, nbytes)
+    dcus = NUM_CUS - pcus
+    if one_grid:
+        # one launch: both sides on the whole chip, the decode side with the
+        # prefill side's worker count (header word 16); the split only says
+        # which workgroup slots of each XCD start with decode
+        ip = sub(pre, NUM_CUS, workers=NUM_CUS * wg_per_cu(D))
+        idc = sub(dec, NUM_CUS, workers=ip[16])
+        first_decode = dcus // NUM_XCDS * wg_per_cu(D)
+    else:
+        ip, idc = sub(pre, pcus), sub(dec, dcus)
+        first_decode = 0
     align = lambda w: _cdiv(w, 64) * 64
     off_d = 64 + align(len(ip))
     partial, part_lse = ip[10], ip[17]
     float_ws_p = max(256, part_lse * 4 + _cdiv(partial * 4, 256) * 256)  # at least 256 bytes
-    hdr = [0x4d414b50, 2, 64, off_d, _cdiv(float_ws_p, 256) * 256 // 4, pcus, NUM_CUS - pcus, B,
-           0 if ragged else kv_indptr[B]]
+    hdr = [0x4d414b50, 2, 64, off_d, _cdiv(float_ws_p, 256) * 256 // 4, pcus, dcus, B,
+           0 if ragged else kv_indptr[B], int(one_grid), first_decode]
     img = hdr + [0] * (64 - len(hdr)) + ip + [0] * (off_d - 64 - len(ip)) + idc
     return img
 
@@ -550,29 +561,39 @@ def _mixed_random(seed):
                    pool_slack=0.2, poison=False)
 
 
+MIXED_MODES = [pka.PKA_MIXED_BATCH | pka.PKA_MIXED_TWO_LAUNCHES, pka.PKA_MIXED_BATCH]
+
+
+@pytest.mark.parametrize("flags", MIXED_MODES, ids=["two_launches", "one_grid"])
 @pytest.mark.parametrize("seed", range(16))
-def test_mixed_restatement(seed):
+def test_mixed_restatement(seed, flags):
     w = _mixed_random(seed)
-    flags = pka.PKA_MIXED_BATCH
     img, info = _image(w, flags)
     want = restate_mixed(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
                          w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size, w.causal,
                          flags, D=w.head_dim)
     assert img.tolist() == want
     assert info["kernel"] == pka.PKA_KERNEL_MIXED
+    if not flags & pka.PKA_MIXED_TWO_LAUNCHES:
+        # one launch: every workgroup serves both images, so both have the launch's worker count
+        h = img[:64].tolist()
+        pre, dec = img[h[2]:h[3]], img[h[3]:]
+        assert h[9] == 1 and int(pre[16]) == int(dec[16]) == info["num_workers"] == NUM_CUS * wg_per_cu(w.head_dim)
+        assert h[10] == info["decode_cus"] // NUM_XCDS * wg_per_cu(w.head_dim)
     assert info["prefill_cus"] + info["decode_cus"] == NUM_CUS and info["prefill_cus"] % NUM_XCDS == 0
     a, b = pka.workspace_size(w.qo_indptr, w.kv_indptr, w.kv_last_page_len, w.num_qo_heads, w.num_kv_heads,
                               w.head_dim, w.page_size, w.causal, flags)
     assert a == info["int_ws_bytes"] == img.numel() * 4 and b == info["float_ws_bytes"]
 
 
+@pytest.mark.parametrize("flags", MIXED_MODES, ids=["two_launches", "one_grid"])
 @pytest.mark.parametrize("seed", range(16))
-def test_mixed_coverage(seed):
+def test_mixed_coverage(seed, flags):
     """Both sub-plans together cover every visible (request, head, row, key)
     once: prefill requests only in the prefill image, decode requests only in
     the decode image (each sub-request is mapped back through its row offset)."""
     w = _mixed_random(seed)
-    img, _ = _image(w, pka.PKA_MIXED_BATCH)
+    img, _ = _image(w, flags)
     h = img[:64].tolist()
     by_row = {int(w.qo_indptr[r]): r for r in range(w.batch) if w.qo_lens[r] > 0}
     G = w.num_qo_heads // w.num_kv_heads
@@ -633,3 +654,10 @@ def test_mixed_cu_split_extremes():
 def test_mixed_rejects_graph_stable():
     w = W.mixed_batch(num_decode=4, num_prefill=1, prefix_range=(10, 40), chunk_range=(5, 9))
     _expect(pka.PKA_ERR_UNSUPPORTED, lambda: _image(w, pka.PKA_MIXED_BATCH | pka.PKA_GRAPH_STABLE))
+    _expect(pka.PKA_ERR_UNSUPPORTED,
+            lambda: _image(w, pka.PKA_MIXED_BATCH | pka.PKA_MIXED_TWO_LAUNCHES | pka.PKA_GRAPH_STABLE))
+
+
+def test_two_launches_needs_the_mixed_flag():
+    w = W.mixed_batch(num_decode=4, num_prefill=1, prefix_range=(10, 40), chunk_range=(5, 9))
+    _expect(pka.PKA_ERR_INVALID_ARG, lambda: _image(w, pka.PKA_MIXED_TWO_LAUNCHES))
