@@ -3,7 +3,9 @@ against pka_run (partial states in the plan's float workspace), through the
 C ABI: the same kernels, so bit-identical outputs, and both within tolerance
 of the CPU oracle.  Two calls in a row on one GPU, the second with a smaller
 batch, so the second reads a scratch the first left behind; plus a plan
-whose partial states exceed the scratch, which must be refused."""
+whose partial states exceed the scratch, which must be refused.  A mixed
+prefill + decode batch goes through the same entry point (in one launch, and
+as two launches)."""
 import os
 
 import pytest
@@ -16,11 +18,11 @@ from tests.gpu_common import compare, cuda, oracle_paged
 pytestmark = pytest.mark.gpu
 
 
-def _both(w):
+def _both(w, **kw):
     dev = cuda()
     plan = pka.Plan(w.qo_indptr, w.kv_indptr, w.kv_indices, w.kv_last_page_len, w.num_qo_heads, w.num_kv_heads,
                     w.head_dim, w.page_size, causal=w.causal, sm_scale=w.sm_scale, num_pages=w.num_pages,
-                    device=dev)
+                    device=dev, **kw)
     q, pool = w.q.to(dev), w.paged_kv.to(dev)
     shape = (w.total_q, w.num_qo_heads, w.head_dim)
     o1 = torch.full(shape, 7.0, dtype=torch.bfloat16, device=dev)
@@ -41,7 +43,13 @@ CASES = [
     # prefill with split KV (few row blocks), then a smaller one
     ("prefill", lambda: W.gqa_append(seed=303, batch=2, prefix_range=(3000, 6000), chunk_range=(100, 300)),
      lambda: W.gqa_append(seed=304, batch=1, prefix_range=(500, 900), chunk_range=(20, 60))),
+    # a mixed prefill + decode batch (its decode requests split KV), then a smaller one
+    ("mixed", lambda: W.mixed_batch(seed=306, num_prefill=2, num_decode=24, prefix_range=(500, 2000),
+                                    chunk_range=(100, 300)),
+     lambda: W.mixed_batch(seed=307, num_prefill=1, num_decode=8, prefix_range=(100, 400), chunk_range=(20, 60))),
 ]
+PLAN_KW = {"decode": {}, "prefill": {}, "mixed": {"mixed": True}, "mixed_two_launches": {"mixed_two_launches": True}}
+CASES.append(("mixed_two_launches", CASES[2][1], CASES[2][2]))
 
 
 @pytest.mark.parametrize("name,big,small", CASES, ids=[c[0] for c in CASES])
@@ -49,7 +57,7 @@ def test_noalloc_matches_run_twice(name, big, small):
     for i, make in enumerate((big, small)):
         w = make()
         print(f"noalloc {name} call {i}: batch={w.batch} total_q={w.total_q}", flush=True)
-        o1, l1, o2, l2, info = _both(w)
+        o1, l1, o2, l2, info = _both(w, **PLAN_KW[name])
         assert info["num_merge_groups"] > 0, "the case must split KV"
         assert torch.equal(o1.view(torch.int16), o2.view(torch.int16)), (name, i)
         assert torch.equal(l1.view(torch.int32), l2.view(torch.int32)), (name, i)
