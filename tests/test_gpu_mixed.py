@@ -221,3 +221,47 @@ def test_one_grid_full_size():
     idx = torch.as_tensor(rows)
     err = compare(o[idx], lse[idx], ref_o, ref_l, "one grid mixed_batch")
     print(f"one grid mixed_batch: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
+
+
+def _subset(w, reqs):
+    """Requests reqs of w as a batch of their own over w's pool: the index
+    arrays and the rows of q (and of the whole batch's outputs) they cover."""
+    qo, kv, idx, last, rows = [0], [0], [], [], []
+    for r in reqs:
+        a, b = int(w.kv_indptr[r]), int(w.kv_indptr[r + 1])
+        qo.append(qo[-1] + int(w.qo_lens[r]))
+        kv.append(kv[-1] + b - a)
+        idx += w.kv_indices[a:b].tolist()
+        last.append(int(w.kv_last_page_len[r]))
+        rows += list(range(int(w.qo_indptr[r]), int(w.qo_indptr[r + 1])))
+    return qo, kv, idx, last, rows
+
+
+@pytest.mark.parametrize("kw", [{"mixed": True}, {"mixed_two_launches": True}], ids=["one_grid", "two_launches"])
+def test_mixed_plan_update_across_kinds(kw):
+    """One mixed-batch plan updated from a mixed batch to a decode-only batch,
+    a prefill-only batch and another mixed batch of the same pool: every run
+    against the oracle rows of its requests."""
+    w = _mixed(9)
+    ref_o, ref_l = oracle_paged(w)
+    pre = [r for r in range(w.batch) if w.qo_lens[r] > 1]
+    dec = [r for r in range(w.batch) if w.qo_lens[r] == 1]
+    batches = [list(range(w.batch)), dec, pre, pre[: max(1, len(pre) // 2)] + dec[::2]]
+    plan = None
+    q_all, pool = w.q.to(cuda()), w.paged_kv.to(cuda())
+    for i, reqs in enumerate(batches):
+        qo, kv, idx, last, rows = _subset(w, reqs)
+        print(f"update {i}: {len(reqs)} requests, {len(rows)} rows", flush=True)
+        if plan is None:
+            plan = pka.Plan(qo, kv, idx, last, w.num_qo_heads, w.num_kv_heads, w.head_dim, w.page_size,
+                            causal=w.causal, sm_scale=w.sm_scale, num_pages=w.num_pages, device=cuda(),
+                            int_ws_bytes=1 << 22, float_ws_bytes=1 << 26, **kw)
+        else:
+            plan.update(qo, kv, idx, last)
+        kinds = {pka.PKA_KERNEL_PREFILL, pka.PKA_KERNEL_DECODE} if i in (1, 2) else {pka.PKA_KERNEL_MIXED}
+        assert plan.info["kernel"] in kinds
+        o, lse = plan.run(q_all[rows], pool)
+        torch.cuda.synchronize()
+        idx_t = torch.as_tensor(rows)
+        compare(o.float().cpu(), lse.cpu(), ref_o[idx_t], ref_l[idx_t], f"update {i}")
+    plan.close()
