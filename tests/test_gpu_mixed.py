@@ -265,3 +265,17 @@ def test_mixed_plan_update_across_kinds(kw):
         idx_t = torch.as_tensor(rows)
         compare(o.float().cpu(), lse.cpu(), ref_o[idx_t], ref_l[idx_t], f"update {i}")
     plan.close()
+
+
+@pytest.mark.parametrize("kw", [{"mixed": True}, {"mixed_two_launches": True}], ids=["one_grid", "two_launches"])
+@pytest.mark.parametrize("D,ps", [(128, 16), (64, 3)])
+def test_mixed_edge_requests(kw, D, ps):
+    """Mixed batches holding the edge cases of both kinds: a decode request
+    with no key, causal prefill rows that see no key (qo_len > kv_len), an
+    empty request, single-key requests, and one long chunk (split KV)."""
+    qo = [1, 5, 0, 1, 300, 1, 2, 1]
+    kv = [0, 3, 10, 1, 2000, 3000, 1, 17]
+    w = W.build("mixed_edges", 777 + D + ps, qo, kv, 8, 2, D, ps, causal=True, pool_slack=0.3)
+    o, lse, info = _run(w, **kw)
+    assert info["kernel"] == pka.PKA_KERNEL_MIXED
+    compare(o.float(), lse, *oracle_paged(w), f"mixed edges {kw} D{D} ps{ps}")
