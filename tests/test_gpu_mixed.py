@@ -202,11 +202,13 @@ def test_one_grid_ragged():
     compare(o.float().cpu(), lse.cpu(), *oracle_paged(w), "one grid ragged")
 
 
-def test_one_grid_full_size():
-    """The chunked-prefill serving step as the benchmark runs it, in one
-    launch: sampled prefill rows (with every request's first and last row)
-    and every decode row against the oracle."""
-    w = W.mixed_batch(device=cuda())
+@pytest.mark.parametrize("D", [128, 64])
+def test_one_grid_full_size(D):
+    """The chunked-prefill serving step as the benchmark runs it (and at
+    head_dim 64, where the decode worker keeps its 4 waves), in one launch:
+    sampled prefill rows (with every request's first and last row) and every
+    decode row against the oracle."""
+    w = W.mixed_batch(device=cuda(), head_dim=D)
     plan = _plan(w, mixed=True)
     assert plan.info["kernel"] == pka.PKA_KERNEL_MIXED
     o, lse = plan.run(w.q, w.paged_kv)
@@ -215,12 +217,12 @@ def test_one_grid_full_size():
     o, lse = o.float().cpu(), lse.cpu()
     dec = [int(w.qo_indptr[r]) for r in range(w.batch) if w.qo_lens[r] == 1]
     ends = [x for r in range(w.batch) if w.qo_lens[r] > 1 for x in (int(w.qo_indptr[r]), int(w.qo_indptr[r + 1]) - 1)]
-    rows = sample_rows(w.total_q, 512, 37, must=dec + ends)
+    rows = sample_rows(w.total_q, 512, 37 + D, must=dec + ends)
     wc = W.Workload(**{**w.__dict__, "q": w.q.cpu(), "paged_kv": w.paged_kv.cpu()})
     ref_o, ref_l = oracle_paged(wc, rows=rows)
     idx = torch.as_tensor(rows)
-    err = compare(o[idx], lse[idx], ref_o, ref_l, "one grid mixed_batch")
-    print(f"one grid mixed_batch: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
+    err = compare(o[idx], lse[idx], ref_o, ref_l, f"one grid mixed_batch D{D}")
+    print(f"one grid mixed_batch D{D}: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
 
 
 def _subset(w, reqs):
