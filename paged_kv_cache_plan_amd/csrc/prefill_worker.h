@@ -190,23 +190,20 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
 
   auto page_of = [&](int key) { return pow2 ? (key >> pshift) : (key / ps); };
   auto slot_of = [&](int key) { return pow2 ? (key & (ps - 1)) : (key - (key / ps) * ps); };
+  // Keys past the unit's range (the last tile's tail) are read as the
+  // range's last key: real, finite rows whose scores the mask removes, so
+  // that no load needs a branch.  kv_hi > kv_lo wherever a tile is fetched.
   auto fetch_ids = [&](const UnitInfo& U, int k0, int* ids) {
     if constexpr (PAGED) {
       const int32_t* idx = pv.kv_indices + U.kv_base;
-      const int key0 = k0 + KPT * lj;
+      const int key0 = k0 + KPT * lj, last = U.kv_hi - 1;
       if constexpr (one_page) {
-        ids[0] = key0 < U.kv_hi ? idx[key0 >> pshift] : 0;
+        ids[0] = idx[min(key0, last) >> pshift];  // a clamped run stays in its page
       } else if constexpr (pair_ids) {
-        const int mine = key0 + (lc & 1);  // page_size 1: page = key
-        ids[0] = mine < U.kv_hi ? idx[mine] : 0;
+        ids[0] = idx[min(key0 + (lc & 1), last)];  // page_size 1: page = key
       } else {
-        const bool full = k0 + kBN <= U.kv_hi;  // uniform
 #pragma unroll
-        for (int i = 0; i < KPT; ++i) {
-          int id = 0;
-          if (full || key0 + i < U.kv_hi) id = idx[page_of(key0 + i)];
-          ids[i < NID ? i : 0] = id;
-        }
+        for (int i = 0; i < KPT; ++i) ids[i < NID ? i : 0] = idx[page_of(min(key0 + i, last))];
       }
     }
   };
@@ -251,13 +248,9 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
     } else {
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
-        kreg[i] = u32x4{0, 0, 0, 0};
-        vreg[i] = u32x4{0, 0, 0, 0};
-        if (key0 + i < U.kv_hi) {
-          const uint64_t off = row_off(U, key0 + i, ids[one_page ? 0 : i]);  // pair_ids: ids = pair
-          kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
-          vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
-        }
+        const uint64_t off = row_off(U, min(key0 + i, U.kv_hi - 1), ids[one_page ? 0 : i]);  // pair_ids: ids = pair
+        kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off);
+        vreg[i] = *reinterpret_cast<const u32x4*>(vbase + off);
       }
     }
   };
