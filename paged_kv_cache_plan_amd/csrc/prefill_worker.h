@@ -313,8 +313,12 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
     f32x16 o[DB];
 #pragma unroll
     for (int b = 0; b < DB; ++b) o[b] = f32x16{};
+    // per row (lane): the reference max m_run (base 2), -m_run for the
+    // exponentials (0 before the row's first visible key), and thr, the raw
+    // score above which the reference moves (sm_scale > 0)
     float m_run = -INFINITY, l_run = 0.f;
-    const float sl2 = a.scale_log2;
+    float neg_m = 0.f, thr = -INFINITY;
+    const float sl2 = a.scale_log2, inv_sl2 = 1.f / sl2;
 
     const int n_tiles = kv_hi > kv_lo ? (kv_hi - kv_lo + kBN - 1) / kBN : 0;
     if (n_tiles == 0) {
@@ -380,19 +384,23 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
         // The reference max moves only when this tile's max exceeds it by
         // more than kSlack (base-2 units): p then stays below 2^kSlack and
         // the O rescale below is rare after a row's first tile.
-        const float m_tile = mx * sl2;
-        const bool bump = m_tile > m_run + kSlack;
-        const float m_new = bump ? m_tile : m_run;
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = (bump && m_run != -INFINITY) ? fast_exp2(m_run - m_new) : 1.f;
+        const bool bump = mx > thr;
+        float alpha = 1.f;
+        if (__any(bump)) {  // the reference moves for some row of this wave
+          const float m_new = bump ? mx * sl2 : m_run;
+          alpha = (bump && m_run != -INFINITY) ? fast_exp2(m_run - m_new) : 1.f;
+          m_run = m_new;
+          neg_m = m_new == -INFINITY ? 0.f : -m_new;
+          thr = (m_new + kSlack) * inv_sl2;
+          if (__any(alpha != 1.f)) {
+#pragma unroll
+            for (int b = 0; b < DB; ++b) o[b] *= alpha;
+          }
+        }
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], sl2, -m_use));
-        if (__any(alpha != 1.f)) {  // the running max moved for some row of this wave
-#pragma unroll
-          for (int b = 0; b < DB; ++b) o[b] *= alpha;
-        }
+          for (int i = 0; i < 16; ++i) s[kb][i] = fast_exp2(__builtin_fmaf(s[kb][i], sl2, neg_m));
 
         // O^T += V^T . P^T, 16 keys per step.  The row sum is taken from the
         // same bf16-rounded p that multiply V, two per v_dot2 (each packed
@@ -418,7 +426,6 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
           }
         }
         l_run = l_run * alpha + rs;
-        m_run = m_new;
       }
       __syncthreads();
     }
