@@ -128,6 +128,12 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
   // Byte offsets: a page's base is one 32x32 -> 64-bit multiply-add.
   const uint32_t page_bytes = static_cast<uint32_t>(a.page_stride) * 2u;
   const uint32_t row_bytes = static_cast<uint32_t>(a.row_stride) * 2u;
+  // Tiles start at multiples of 64 keys, so with power-of-two pages the slot
+  // of a loader thread's first key is a lane part (below) plus a tile part.
+  // (opaque, so that the compiler does not fold the two parts' products
+  // back into one multiply per tile)
+  uint32_t lane_slot_bytes = static_cast<uint32_t>((KPT * lj) & (min(ps, kBN) - 1)) * row_bytes;
+  asm volatile("" : "+v"(lane_slot_bytes));
   // A power-of-two page_size >= KPT keeps a thread's KPT keys (KPT-aligned,
   // tiles start 64-aligned) in one page: one page id per thread per tile.
   constexpr bool one_page = MODE == kKvPagedRun;
@@ -231,7 +237,8 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
     const int key0 = k0 + KPT * lj;
     if (k0 + kBN <= U.kv_hi) {  // uniform: the whole tile is in range
       if constexpr (one_page) {
-        const uint64_t off0 = row_off(U, key0, ids[0]);
+        const uint32_t slot_bytes = lane_slot_bytes + static_cast<uint32_t>(k0 & (ps - 1) & ~(kBN - 1)) * row_bytes;
+        const uint64_t off0 = static_cast<uint64_t>(static_cast<uint32_t>(ids[0])) * page_bytes + slot_bytes;
 #pragma unroll
         for (int i = 0; i < KPT; ++i) {
           kreg[i] = *reinterpret_cast<const u32x4*>(kbase + off0 + i * row_bytes);
@@ -374,19 +381,21 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
             for (int i = 0; i < 16; ++i)
               if (kb * 32 + 8 * (i >> 2) + (i & 3) > thr) s[kb][i] = -INFINITY;
         }
-        // online softmax in base 2
+        // online softmax in base 2: the max of this lane's half of the row
         float mx = -INFINITY;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
           for (int i = 0; i < 16; ++i) mx = fmaxf(mx, s[kb][i]);
-        mx = xor32_max(mx);
         // The reference max moves only when this tile's max exceeds it by
         // more than kSlack (base-2 units): p then stays below 2^kSlack and
-        // the O rescale below is rare after a row's first tile.
-        const bool bump = mx > thr;
+        // the O rescale below is rare after a row's first tile.  Either half
+        // shows whether a row moves; the row max (lanes l and l ^ 32) is
+        // taken only then.
         float alpha = 1.f;
-        if (__any(bump)) {  // the reference moves for some row of this wave
+        if (__any(mx > thr)) {  // the reference moves for some row of this wave
+          mx = xor32_max(mx);
+          const bool bump = mx > thr;
           const float m_new = bump ? mx * sl2 : m_run;
           alpha = (bump && m_run != -INFINITY) ? fast_exp2(m_run - m_new) : 1.f;
           m_run = m_new;
