@@ -89,6 +89,25 @@ def test_append_skips_invalid_entries():
     assert torch.equal(pool.view(torch.int16), ref.view(torch.int16))
 
 
+@pytest.mark.parametrize("batch", [1, 4096, 5000])
+def test_batch_indices_positions_many_requests(batch):
+    """One request, and thousands of requests (a binary search over
+    append_indptr per token), with empty requests: indices and positions
+    bit-exact."""
+    dev = cuda()
+    g = torch.Generator().manual_seed(batch)
+    n = torch.randint(0, 4, (batch,), generator=g)
+    n[::7] = 0
+    if batch == 1:
+        n[0] = 3
+    indptr = torch.zeros(batch + 1, dtype=torch.int32)
+    indptr[1:] = torch.cumsum(n, 0).to(torch.int32)
+    seq = (n + torch.randint(0, 50, (batch,), generator=g)).to(torch.int32)
+    bi, pos = pka.get_batch_indices_positions(indptr.to(dev), seq.to(dev), int(indptr[-1]))
+    rb, rp = A.batch_indices_positions(indptr, seq)
+    assert torch.equal(bi.cpu(), rb) and torch.equal(pos.cpu(), rp)
+
+
 def test_append_nothing():
     g = torch.Generator().manual_seed(6)
     w = W.build_append("t", 6, [5, 9], [0, 0], 1, 128, 16, gen=g)
