@@ -46,16 +46,26 @@ PEAK_BF16_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 PEAK_HBM_GBS = 8000.0      # MI355X HBM3E
 METRIC = "causal paged prefill TFLOP/s (D=128) and decode HBM GB/s, % of roofline"
 KERNEL_SOURCES = ["prefill_worker.h", "prefill.hip", "decode_worker.h", "decode.hip", "mixed.hip", "merge.hip",
-                  "device.h", "args.h", "planner.h"]
+                  "append.hip", "device.h", "args.h", "planner.h"]
+
+
+def _code_only(text: str) -> str:
+    """C++ source without its // comments and blank lines (the kernel sources
+    have no block comments and no // inside strings)."""
+    lines = (line.split("//", 1)[0].rstrip() for line in text.splitlines())
+    return "\n".join(line for line in lines if line)
 
 
 def kernel_source_hash() -> str:
+    """Hash of the code behind the measured kernels: their sources without
+    comments, and the build script (compile flags), so that an edit to a
+    comment does not mark profiles/traffic.json as stale."""
     h = hashlib.sha256()
-    paths = [os.path.join(ROOT, "paged_kv_cache_plan_amd", "csrc", f) for f in KERNEL_SOURCES]
-    paths.append(os.path.join(ROOT, "paged_kv_cache_plan_amd", "build.py"))  # compile flags
-    for path in paths:
-        with open(path, "rb") as fh:
-            h.update(fh.read())
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_plan_amd", "csrc", f)) as fh:
+            h.update(_code_only(fh.read()).encode())
+    with open(os.path.join(ROOT, "paged_kv_cache_plan_amd", "build.py"), "rb") as fh:
+        h.update(fh.read())
     return h.hexdigest()[:16]
 
 

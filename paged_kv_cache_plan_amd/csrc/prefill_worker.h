@@ -26,10 +26,13 @@
 //   S^T      = K . Q^T with v_mfma_f32_32x32x16_bf16: each wave owns 32 query
 //            rows as MFMA columns, so a lane holds 16 of a row's 32 scores per
 //            32-key block and the other 16 sit in lane l ^ 32.
-//   softmax  online, fp32, base 2 (sm_scale * log2 e folded into one FMA);
-//            row max needs one v_permlane32_swap; the row sum adds the
-//            bf16-rounded p that multiply V, two per v_dot2, and stays per
-//            lane until the end.
+//   softmax  online, fp32, base 2 (sm_scale * log2 e folded into one FMA)
+//            against a reference max that moves only when a tile's max
+//            exceeds it by more than kSlack; each lane compares its half of
+//            the row with a per-row bound, and the halves' max is exchanged
+//            (v_permlane32_swap) only when some row moves.  The row sum adds
+//            the bf16-rounded p that multiply V, two per v_dot2, and stays
+//            per lane until the end.
 //   O^T     += V^T . P^T with the same MFMA; P^T is the S^T accumulator
 //            rounded to bf16 in place (no data movement), V^T comes from LDS.
 #pragma once
