@@ -1,6 +1,8 @@
 """GPU parity: the HIP path (through the C ABI) against the CPU fp64 oracle on
 the same seeded inputs, at sizes the oracle finishes in seconds that still
 span several tiles and ragged tails, plus the edge cases of the method."""
+import math
+
 import pytest
 import torch
 
@@ -209,6 +211,49 @@ def test_edge_cases():
     w = W.build("edge", 3, [3, 0, 70, 1], [0, 5, 20, 1], 4, 2, 64, 4, causal=True, pool_slack=0.5)
     o, lse, _ = run_paged(w)
     compare(o, lse, *oracle_paged(w), "edge")
+
+
+def _growing_keys(w, top=5.0):
+    """A copy of w whose K rows are scaled by 1 at key 0 up to `top` at each
+    request's last key, so that a row's largest logits come late."""
+    pool = w.paged_kv.clone()
+    ps = w.page_size
+    for r in range(w.batch):
+        n = int(w.kv_indptr[r + 1] - w.kv_indptr[r])
+        kv = int((n - 1) * ps + w.kv_last_page_len[r]) if n else 0
+        for j, pid in enumerate(w.kv_indices[int(w.kv_indptr[r]):int(w.kv_indptr[r + 1])].tolist()):
+            pos = torch.arange(j * ps, (j + 1) * ps, dtype=torch.float32)
+            f = (1.0 + (top - 1.0) * pos / max(kv, 1)).clamp(max=top)
+            pool[pid, 0] = (pool[pid, 0].float() * f[:, None, None]).to(torch.bfloat16)
+    w.paged_kv = pool
+    return w
+
+
+@pytest.mark.parametrize("decode", [False, True])
+def test_reference_max_moves_late(decode):
+    """K rows scaled up along each sequence (x1 to x5), so that a row's max
+    logit rises by more than the rescale slack after its first tiles: the
+    softmax reference moves, and O and the row sum are rescaled, in the
+    middle of a row's keys, not only on its first tile."""
+    qo = [1, 1, 1] if decode else [700, 300, 64]
+    kv = [2000, 1500, 4096]
+    w = _growing_keys(W.build(f"growing_{decode}", 61, qo, kv, 8, 2, 128, 16, causal=True))
+    # premise: for the last request, the last tile's max logit (base 2) is
+    # more than 8 above the first tile's for most (row, head) pairs
+    r = 2
+    q = w.q[int(w.qo_indptr[r]):int(w.qo_indptr[r + 1])].double()
+    pages = w.kv_indices[int(w.kv_indptr[r]):int(w.kv_indptr[r + 1])]
+    k = w.paged_kv[pages, 0].reshape(-1, w.num_kv_heads, w.head_dim)[:kv[r]].double()
+    G = w.num_qo_heads // w.num_kv_heads
+    s = torch.einsum("qhd,khd->hqk", q, k.repeat_interleave(G, dim=1)) * w.sm_scale / math.log(2.0)
+    rise = s[:, :, -64:].amax(-1) - s[:, :, :64].amax(-1)
+    assert (rise > 8).float().mean() > 0.5, rise
+    for split in (True, False):
+        o, lse, info = run_paged(w, disable_split_kv=not split)
+        assert info["kernel"] == (pka.PKA_KERNEL_DECODE if decode else pka.PKA_KERNEL_PREFILL)
+        err = compare(o, lse, *oracle_paged(w), f"growing keys decode={decode} split={split}")
+        print(f"growing keys decode={decode} split={split}: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}",
+              flush=True)
 
 
 @pytest.mark.parametrize("ps", [1, 16])
