@@ -256,6 +256,22 @@ def test_reference_max_moves_late(decode):
               flush=True)
 
 
+@pytest.mark.parametrize("sm_scale", [0.02, 0.5])
+@pytest.mark.parametrize("decode", [False, True])
+@pytest.mark.parametrize("D", [64, 128])
+def test_explicit_sm_scale(sm_scale, decode, D):
+    """sm_scale given by the caller instead of 1/sqrt(D): a nearly flat
+    softmax (0.02) and a sharp one (0.5, logits with a standard deviation of
+    about 8 base-2 units at D=128)."""
+    qo = [1, 1, 1, 1] if decode else [200, 33, 1, 90]
+    w = W.build(f"scale_{sm_scale}_{decode}_{D}", 71, qo, [300, 33, 900, 150], 8, 2, D, 16, causal=True)
+    w.sm_scale = sm_scale
+    o, lse, info = run_paged(w)
+    assert info["kernel"] == (pka.PKA_KERNEL_DECODE if decode else pka.PKA_KERNEL_PREFILL)
+    err = compare(o, lse, *oracle_paged(w), f"sm_scale={sm_scale} decode={decode} D={D}")
+    print(f"sm_scale={sm_scale} decode={decode} D={D}: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
+
+
 @pytest.mark.parametrize("ps", [1, 16])
 def test_decode_empty_kv(ps):
     """Decode requests with no keys (kv_len 0) next to short ones: (0, -inf)
