@@ -374,15 +374,15 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
         }
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, 4, 0);
         // mask: keys past the unit's range, and (causal) keys past the row's
-        // limit; thr = last visible key offset in this tile for the lane's row
+        // limit; lim_t = last visible key offset in this tile for the lane's row
         const bool need_mask = (k0 + kBN > kv_hi) || (CAUSAL && k0 + kBN - 1 > wave_lim);
         if (need_mask) {
-          const int thr = (CAUSAL ? min(lim, kv_hi - 1) : kv_hi - 1) - k0 - 4 * half;
+          const int lim_t = (CAUSAL ? min(lim, kv_hi - 1) : kv_hi - 1) - k0 - 4 * half;
 #pragma unroll
           for (int kb = 0; kb < 2; ++kb)
 #pragma unroll
             for (int i = 0; i < 16; ++i)
-              if (kb * 32 + 8 * (i >> 2) + (i & 3) > thr) s[kb][i] = -INFINITY;
+              if (kb * 32 + 8 * (i >> 2) + (i & 3) > lim_t) s[kb][i] = -INFINITY;
         }
         // online softmax in base 2: the max of this lane's half of the row
         float mx = -INFINITY;
