@@ -131,15 +131,18 @@ __device__ __forceinline__ void prefill_worker(const AttnArgs a) {
   // Byte offsets: a page's base is one 32x32 -> 64-bit multiply-add.
   const uint32_t page_bytes = static_cast<uint32_t>(a.page_stride) * 2u;
   const uint32_t row_bytes = static_cast<uint32_t>(a.row_stride) * 2u;
-  // Tiles start at multiples of 64 keys, so with power-of-two pages the slot
-  // of a loader thread's first key is a lane part (below) plus a tile part.
-  // (opaque, so that the compiler does not fold the two parts' products
-  // back into one multiply per tile)
-  uint32_t lane_slot_bytes = static_cast<uint32_t>((KPT * lj) & (min(ps, kBN) - 1)) * row_bytes;
-  asm volatile("" : "+v"(lane_slot_bytes));
   // A power-of-two page_size >= KPT keeps a thread's KPT keys (KPT-aligned,
   // tiles start 64-aligned) in one page: one page id per thread per tile.
   constexpr bool one_page = MODE == kKvPagedRun;
+  // With such pages the slot of a loader thread's first key is a lane part
+  // (below) plus a tile part, since tiles start at multiples of 64 keys.
+  // (opaque, so that the compiler does not fold the two parts' products
+  // back into one multiply per tile)
+  uint32_t lane_slot_bytes = 0;
+  if constexpr (one_page) {
+    lane_slot_bytes = static_cast<uint32_t>((KPT * lj) & (min(ps, kBN) - 1)) * row_bytes;
+    asm volatile("" : "+v"(lane_slot_bytes));
+  }
   // Single-key pages with KPT == 2: the two lanes of a pair load one page id
   // each and swap them with one DPP move.
   constexpr bool pair_ids = MODE == kKvPagedPow2 && KPT == 2;
