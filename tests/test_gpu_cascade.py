@@ -147,3 +147,49 @@ def test_cascade_head_dim_64_group_3(qo):
     torch.cuda.synchronize()
     c.close()
     compare(o.float().cpu(), lse.cpu(), *_oracle(pool, q, tables, qo_indptr, True, ps), f"cascade D=64 G=3 {qo}")
+
+
+def _random_cascade(seed):
+    g = torch.Generator().manual_seed(4000 + seed)
+    pick = lambda xs: xs[int(torch.randint(0, len(xs), (1,), generator=g))]
+    B = int(torch.randint(2, 7, (1,), generator=g))
+    decode = seed % 3 == 0
+    qo_lens = [1] * B if decode else [int(torch.randint(1, 60, (1,), generator=g)) for _ in range(B)]
+    causal = bool(torch.rand(1, generator=g) < 0.7)
+    groups = [[list(range(B))]]
+    lens = [[int(torch.randint(0, 400, (1,), generator=g))]]
+    if torch.rand(1, generator=g) < 0.5:  # a middle level over contiguous groups of requests
+        cuts = sorted(set(int(c) for c in torch.randint(1, B, (int(torch.randint(0, 3, (1,), generator=g)),),
+                                                        generator=g).tolist()))
+        bounds = [0] + cuts + [B]
+        groups.append([list(range(a, b)) for a, b in zip(bounds, bounds[1:])])
+        lens.append([int(torch.randint(0, 150, (1,), generator=g)) for _ in groups[-1]])
+    if seed % 4 == 2:  # an empty shared level
+        lens[0][0] = 0
+    if len(lens) > 1 and seed % 5 == 1:  # an empty group in the middle level
+        lens[1][0] = 0
+    groups.append([[r] for r in range(B)])
+    own = [int(torch.randint(0, 200, (1,), generator=g)) for _ in range(B)]
+    if causal:  # the last level holds at least each request's query rows
+        own = [max(o, n) for o, n in zip(own, qo_lens)]
+    lens.append(own)
+    shape = dict(ps=pick([1, 3, 16]), Hq=0, Hkv=pick([1, 2]), D=pick([64, 128]))
+    shape["Hq"] = shape["Hkv"] * pick([1, 3, 4])
+    return groups, lens, qo_lens, causal, shape, bool(torch.rand(1, generator=g) < 0.3)
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_cascade(seed):
+    """Seeded random cascades: two or three levels, random group splits,
+    empty levels, decode or prefill rows, causal or not, page sizes 1, 3
+    and 16, D=64 and 128, bf16 or fp32 output."""
+    groups, lens, qo_lens, causal, shape, fp32 = _random_cascade(seed)
+    print(f"case {seed}: groups={groups} lens={lens} qo={qo_lens} causal={causal} {shape} fp32={fp32}", flush=True)
+    pool, q, levels, tables, qo_indptr, num_pages, (Hq, Hkv, D, ps) = _build(50 + seed, groups, lens, qo_lens,
+                                                                             **shape)
+    dev = cuda()
+    c = pka.Cascade(levels, Hq, Hkv, D, ps, causal=causal, num_pages=num_pages, out_fp32=fp32, device=dev)
+    o, lse = c.run(q.to(dev), pool.to(dev))
+    torch.cuda.synchronize()
+    c.close()
+    compare(o.float().cpu(), lse.cpu(), *_oracle(pool, q, tables, qo_indptr, causal, ps), f"random cascade {seed}")
