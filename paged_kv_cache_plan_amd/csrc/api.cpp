@@ -50,6 +50,7 @@ struct PartLaunch {
   int32_t merge_slices;  // workgroup slices of its largest merge group
   int32_t off_words;  // its image inside the int workspace
   size_t float_off;   // its partial states inside the float workspace (bytes)
+  int32_t wg_per_cu;  // prefill: workgroups per CU planned for (selects the kernel build)
 };
 
 // A pinned host buffer that a plan stages its image in, and the event
@@ -249,12 +250,12 @@ int upload(pka_plan* p, const Planned& pl, int32_t batch, int32_t nnz, hipStream
     const pka::MixedPlan& mp = pl.mp;
     p->num_parts = 2;
     p->parts[0] = {mp.prefill.kernel, mp.prefill.num_workers, mp.prefill.num_merge,
-                   mp.prefill.image[pka::kHdrMergeSlices], mp.off_prefill, 0};
+                   mp.prefill.image[pka::kHdrMergeSlices], mp.off_prefill, 0, mp.prefill.wg_per_cu};
     p->parts[1] = {mp.decode.kernel, mp.decode.num_workers, mp.decode.num_merge,
-                   mp.decode.image[pka::kHdrMergeSlices], mp.off_decode, mp.float_off_decode};
+                   mp.decode.image[pka::kHdrMergeSlices], mp.off_decode, mp.float_off_decode, mp.decode.wg_per_cu};
   } else {
     p->num_parts = 1;
-    p->parts[0] = {res.kernel, res.num_workers, res.num_merge, res.image[pka::kHdrMergeSlices], 0, 0};
+    p->parts[0] = {res.kernel, res.num_workers, res.num_merge, res.image[pka::kHdrMergeSlices], 0, 0, res.wg_per_cu};
   }
   return PKA_OK;
 }
@@ -331,7 +332,7 @@ int run_part(const pka_plan* p, const PartLaunch& part, const void* q, const voi
   if (part.kernel == PKA_KERNEL_DECODE)
     e = pka::launch_decode(a, p->head_dim, paged, part.num_workers, stream);
   else
-    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, part.num_workers, stream);
+    e = pka::launch_prefill(a, p->head_dim, paged, p->causal != 0, part.num_workers, part.wg_per_cu, stream);
   if (e != hipSuccess) return hip_error("attention launch", e);
   return run_merge(p, part, a, o, lse, stream);
 }

@@ -7,7 +7,8 @@
 
 namespace pka {
 
-hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool paged, bool causal, int grid,
+// wg_per_cu: workgroups per CU the plan was made for (selects the build at D=64)
+hipError_t launch_prefill(const AttnArgs& a, int head_dim, bool paged, bool causal, int grid, int wg_per_cu,
                           hipStream_t stream);
 hipError_t launch_decode(const AttnArgs& a, int head_dim, bool paged, int grid, hipStream_t stream);
 // One-grid mixed batch: every workgroup runs the prefill worker and the decode

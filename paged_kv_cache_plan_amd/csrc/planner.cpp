@@ -213,6 +213,12 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   };
   // Queues: queue_begin[q] .. queue_begin[q + 1] index the unit array.
   const bool fixed = (in.flags & kFlagGraphStable) != 0;
+  int wgs = decode ? kDecodeWgPerCu : prefill_wg_per_cu(in.head_dim);
+  if (!decode && in.head_dim == 64 && !fixed && in.workers_override <= 0 && !in.qo_begin && !units.empty()) {
+    int64_t keys = 0;
+    for (const Unit& u : units) keys += u.f[kUnitKvEnd] - u.f[kUnitKvBegin];
+    if (keys >= kPrefillLongUnitKeys * static_cast<int64_t>(units.size())) wgs = kPrefillWgPerCuLong64;
+  }
   std::vector<int32_t> queue_begin{0};
   if (decode) {
     // One queue, longest first: big units start first and small ones fill
@@ -268,7 +274,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
     // workers) run longest-first across groups, so that its workers finish
     // together; this costs some L2 reuse at the end.
     const int64_t slots_per_queue =
-        std::max<int64_t>(1, int64_t(std::max(1, in.num_cus)) * prefill_wg_per_cu(in.head_dim) / X);
+        std::max<int64_t>(1, int64_t(std::max(1, in.num_cus)) * wgs / X);
     const size_t tail = static_cast<size_t>(kQueueTailSlots * slots_per_queue);
     for (int x = 0; x < X; ++x) {
       std::vector<Unit>& q = queue[x];
@@ -288,9 +294,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   const int32_t n_queues = static_cast<int32_t>(queue_begin.size()) - 1;
   int64_t longest = 0;
   for (int q = 0; q < n_queues; ++q) longest = std::max<int64_t>(longest, queue_begin[q + 1] - queue_begin[q]);
-  const int64_t slots = in.workers_override > 0
-                            ? int64_t(in.workers_override)
-                            : int64_t(std::max(1, in.num_cus)) * (decode ? kDecodeWgPerCu : prefill_wg_per_cu(in.head_dim));
+  const int64_t slots = in.workers_override > 0 ? int64_t(in.workers_override) : int64_t(std::max(1, in.num_cus)) * wgs;
   const int64_t per_queue_max = std::max<int64_t>(1, slots / n_queues);
   const int32_t workers_per_queue = static_cast<int32_t>(
       (fixed || in.workers_override > 0) ? per_queue_max
@@ -357,6 +361,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   out->kv_chunk = any_split ? static_cast<int32_t>(chunk) : 0;
   out->num_queues = n_queues;
   out->num_workers = n_workers;
+  out->wg_per_cu = wgs;
   out->total_q = in.qo_indptr[B];
   out->total_kv = total_kv;
   const size_t o_bytes = static_cast<size_t>(partial_rows) * in.head_dim * sizeof(float);

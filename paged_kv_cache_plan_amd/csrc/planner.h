@@ -176,6 +176,13 @@ struct PlanInput {
 constexpr int prefill_waves(int head_dim) { return head_dim == 128 ? 8 : 4; }
 constexpr int prefill_block_rows(int head_dim) { return 32 * prefill_waves(head_dim); }
 constexpr int prefill_wg_per_cu(int head_dim) { return head_dim == 128 ? 1 : 2; }
+// At D=64 a batch whose units average at least kPrefillLongUnitKeys keys is
+// planned for three workgroups per CU, run by a build of the kernel whose
+// launch bound caps it at 168 VGPRs; batches of shorter units keep two (that
+// build loses more to its register cap there than the third workgroup
+// brings).  Graph-stable plans and the sub-plans of a mixed batch keep two.
+constexpr int kPrefillWgPerCuLong64 = 3;
+constexpr int64_t kPrefillLongUnitKeys = 1536;
 
 struct PlanResult {
   int32_t kernel = kPrefill;
@@ -186,6 +193,7 @@ struct PlanResult {
   int32_t kv_chunk = 0;
   int32_t num_queues = 0;   // prefill only
   int32_t num_workers = 0;  // workgroups of the attention launch
+  int32_t wg_per_cu = 0;    // prefill: workgroups per CU the launch is planned (and built) for
   int64_t total_q = 0;
   int64_t total_kv = 0;
   std::vector<int32_t> image;  // the int workspace image

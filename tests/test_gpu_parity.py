@@ -46,6 +46,23 @@ def test_page_sizes_d64(ps):
     compare(o, lse, *oracle_paged(w), f"D=64 ps={ps}")
 
 
+@pytest.mark.parametrize("ps", [16, 1, 3])
+def test_head_dim_64_three_workgroups_per_cu(ps):
+    """A D=64 batch of long units (prefixes of 2000-4000 keys) is planned for
+    three workgroups per CU and run by the build of the kernel made for
+    three; sampled rows (and every request's first and last) against the
+    oracle."""
+    from tests.gpu_common import sample_rows
+    w = W.gqa_append(seed=60 + ps, batch=32, prefix_range=(2000, 4000), chunk_range=(64, 300),
+                     page_size=ps, head_dim=64)
+    o, lse, info = run_paged(w)
+    assert info["kernel"] == pka.PKA_KERNEL_PREFILL and info["num_workers"] > 2 * 256, info["num_workers"]
+    ends = [int(x) for x in w.qo_indptr[:-1]] + [int(x) - 1 for x in w.qo_indptr[1:]]
+    rows = sample_rows(w.total_q, 512, 70 + ps, must=ends)
+    err = compare(o[rows], lse[rows], *oracle_paged(w, rows=rows), f"D=64 three per CU ps={ps}")
+    print(f"D=64 three workgroups per CU, ps={ps}: max |dO| {err[0]:.2e}, max |dlse| {err[1]:.2e}", flush=True)
+
+
 def test_repeat_runs_of_one_plan():
     """Prefill workgroups take units from queues whose counters reset at the
     end of each launch: every run of one plan must redo the whole batch."""

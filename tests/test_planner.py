@@ -33,6 +33,11 @@ def block_rows(D):
 
 def wg_per_cu(D):
     return 1 if D == 128 else 2
+
+
+# At D=64 a batch whose units average at least this many keys is planned for
+# three prefill workgroups per CU (not graph-stable plans or mixed sub-plans).
+LONG_UNIT_KEYS, WG_PER_CU_LONG64 = 1536, 3
 NUM_CUS, NUM_XCDS, QUEUE_WINDOW, QUEUE_TAIL_SLOTS = 256, 8, 2, 2
 UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 16, 8, 8
 
@@ -113,6 +118,10 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
                           (up - lo) * nrows + 1, len(units)))
     key = lambda u: (-u[1], u[2])
     fixed = bool(flags & pka.PKA_GRAPH_STABLE)
+    wgs = 2 if decode else wg_per_cu(D)
+    if (not decode and D == 64 and not fixed and workers <= 0 and qo_begin is None and units
+            and sum(u[0][5] - u[0][4] for u in units) >= LONG_UNIT_KEYS * len(units)):
+        wgs = WG_PER_CU_LONG64
     bounds = [0]  # queue q holds units bounds[q] .. bounds[q + 1]
     if decode or (len(units) <= NUM_XCDS and not fixed):
         units.sort(key=key)
@@ -140,7 +149,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
                   for gs in queues]
         # the last QUEUE_TAIL_SLOTS units per worker slot of a queue run
         # longest-first across its groups (stable: ties keep queue order)
-        tail = QUEUE_TAIL_SLOTS * max(1, num_cus * wg_per_cu(D) // NUM_XCDS)
+        tail = QUEUE_TAIL_SLOTS * max(1, num_cus * wgs // NUM_XCDS)
         queues = [q[:max(0, len(q) - tail)] + sorted(q[max(0, len(q) - tail):], key=lambda v: -v[1])
                   for q in queues]
         queues = [[u[0] for u in q] for q in queues]
@@ -151,7 +160,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     nq = len(bounds) - 1
     longest = max(bounds[q + 1] - bounds[q] for q in range(nq))
     # workers > 0: exactly that many, evenly over the queues (a one-grid mixed launch)
-    slots = workers if workers > 0 else num_cus * (2 if decode else wg_per_cu(D))
+    slots = workers if workers > 0 else num_cus * wgs
     per_queue = max(1, slots // nq) if (fixed or workers > 0) else max(1, min(longest, max(1, slots // nq)))
     workers = nq * per_queue
     align = lambda w: _cdiv(w, 64) * 64
@@ -361,6 +370,33 @@ def test_named_workloads_restatement(name, kw):
     a, b = pka.workspace_size(w.qo_indptr, w.kv_indptr, w.kv_last_page_len, w.num_qo_heads,
                               w.num_kv_heads, w.head_dim, w.page_size, w.causal)
     assert a == info["int_ws_bytes"] and b == info["float_ws_bytes"]
+
+
+@pytest.mark.parametrize("long_units", [True, False])
+@pytest.mark.parametrize("flags", [0, pka.PKA_GRAPH_STABLE])
+def test_head_dim_64_workgroups_per_cu(long_units, flags):
+    """At D=64 a batch of long units (at least 1536 keys each on average) is
+    planned for three prefill workgroups per CU, one of short units for two;
+    graph-stable plans always for two.  The image matches the restatement."""
+    if long_units:
+        w = W.gqa_append(seed=21, batch=32, prefix_range=(2000, 4000), chunk_range=(64, 300), head_dim=64)
+    else:
+        w = W.gqa_append(seed=22, batch=32, prefix_range=(40, 400), chunk_range=(64, 300), head_dim=64)
+    img, info = _image(w, flags=flags)
+    want = restate_plan(w.qo_indptr.tolist(), w.kv_indptr.tolist(), w.kv_indices.tolist(),
+                        w.kv_last_page_len.tolist(), w.num_qo_heads, w.num_kv_heads, w.page_size,
+                        w.causal, flags, D=64)
+    assert img.tolist() == want
+    three = long_units and not flags
+    _, units, _, _, _ = _unpack(img)
+    mean_keys = sum(u[5] - u[4] for u in units) / len(units)
+    assert (mean_keys >= LONG_UNIT_KEYS) == long_units
+    if flags:
+        assert info["num_workers"] == NUM_CUS * 2
+    else:
+        assert info["num_workers"] <= NUM_CUS * (3 if three else 2)
+        if three:
+            assert info["num_workers"] > NUM_CUS * 2 or len(units) <= NUM_CUS * 2
 
 
 def test_ragged_restatement():
