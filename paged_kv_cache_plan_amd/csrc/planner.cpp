@@ -217,7 +217,7 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   if (!decode && in.head_dim == 64 && !fixed && in.workers_override <= 0 && !in.qo_begin && !units.empty()) {
     int64_t keys = 0;
     for (const Unit& u : units) keys += u.f[kUnitKvEnd] - u.f[kUnitKvBegin];
-    if (keys >= kPrefillLongUnitKeys * static_cast<int64_t>(units.size())) wgs = kPrefillWgPerCuLong64;
+    if (keys * G >= kPrefillLongUnitKeys * static_cast<int64_t>(units.size())) wgs = kPrefillWgPerCuLong64;
   }
   std::vector<int32_t> queue_begin{0};
   if (decode) {

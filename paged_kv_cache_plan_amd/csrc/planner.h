@@ -176,13 +176,14 @@ struct PlanInput {
 constexpr int prefill_waves(int head_dim) { return head_dim == 128 ? 8 : 4; }
 constexpr int prefill_block_rows(int head_dim) { return 32 * prefill_waves(head_dim); }
 constexpr int prefill_wg_per_cu(int head_dim) { return head_dim == 128 ? 1 : 2; }
-// At D=64 a batch whose units average at least kPrefillLongUnitKeys keys is
-// planned for three workgroups per CU, run by a build of the kernel whose
-// launch bound caps it at 168 VGPRs; batches of shorter units keep two (that
-// build loses more to its register cap there than the third workgroup
+// At D=64 a batch whose units average at least kPrefillLongUnitKeys keys
+// times the group size (query heads per KV head: the rows that share each
+// K/V tile) is planned for three workgroups per CU, run by a build of the
+// kernel whose launch bound caps it at 168 VGPRs; other batches keep two
+// (that build loses more to its register cap there than the third workgroup
 // brings).  Graph-stable plans and the sub-plans of a mixed batch keep two.
 constexpr int kPrefillWgPerCuLong64 = 3;
-constexpr int64_t kPrefillLongUnitKeys = 1536;
+constexpr int64_t kPrefillLongUnitKeys = 2048;
 
 struct PlanResult {
   int32_t kernel = kPrefill;

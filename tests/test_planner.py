@@ -35,9 +35,10 @@ def wg_per_cu(D):
     return 1 if D == 128 else 2
 
 
-# At D=64 a batch whose units average at least this many keys is planned for
-# three prefill workgroups per CU (not graph-stable plans or mixed sub-plans).
-LONG_UNIT_KEYS, WG_PER_CU_LONG64 = 1536, 3
+# At D=64 a batch whose units average at least this many keys times the group
+# size is planned for three prefill workgroups per CU (not graph-stable plans
+# or mixed sub-plans).
+LONG_UNIT_KEYS, WG_PER_CU_LONG64 = 2048, 3
 NUM_CUS, NUM_XCDS, QUEUE_WINDOW, QUEUE_TAIL_SLOTS = 256, 8, 2, 2
 UNIT_WORDS, REQ_WORDS, MERGE_WORDS = 16, 8, 8
 
@@ -120,7 +121,7 @@ def restate_plan(qo_indptr, kv_indptr, kv_indices, last, Hq, Hkv, ps, causal, fl
     fixed = bool(flags & pka.PKA_GRAPH_STABLE)
     wgs = 2 if decode else wg_per_cu(D)
     if (not decode and D == 64 and not fixed and workers <= 0 and qo_begin is None and units
-            and sum(u[0][5] - u[0][4] for u in units) >= LONG_UNIT_KEYS * len(units)):
+            and sum(u[0][5] - u[0][4] for u in units) * G >= LONG_UNIT_KEYS * len(units)):
         wgs = WG_PER_CU_LONG64
     bounds = [0]  # queue q holds units bounds[q] .. bounds[q + 1]
     if decode or (len(units) <= NUM_XCDS and not fixed):
@@ -375,9 +376,10 @@ def test_named_workloads_restatement(name, kw):
 @pytest.mark.parametrize("long_units", [True, False])
 @pytest.mark.parametrize("flags", [0, pka.PKA_GRAPH_STABLE])
 def test_head_dim_64_workgroups_per_cu(long_units, flags):
-    """At D=64 a batch of long units (at least 1536 keys each on average) is
-    planned for three prefill workgroups per CU, one of short units for two;
-    graph-stable plans always for two.  The image matches the restatement."""
+    """At D=64 a batch of long units (keys per unit times the group size at
+    least 2048 on average) is planned for three prefill workgroups per CU, one
+    of short units for two; graph-stable plans always for two.  The image
+    matches the restatement."""
     if long_units:
         w = W.gqa_append(seed=21, batch=32, prefix_range=(2000, 4000), chunk_range=(64, 300), head_dim=64)
     else:
@@ -390,7 +392,7 @@ def test_head_dim_64_workgroups_per_cu(long_units, flags):
     three = long_units and not flags
     _, units, _, _, _ = _unpack(img)
     mean_keys = sum(u[5] - u[4] for u in units) / len(units)
-    assert (mean_keys >= LONG_UNIT_KEYS) == long_units
+    assert (mean_keys * (w.num_qo_heads // w.num_kv_heads) >= LONG_UNIT_KEYS) == long_units
     if flags:
         assert info["num_workers"] == NUM_CUS * 2
     else:
