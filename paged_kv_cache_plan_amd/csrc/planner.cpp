@@ -213,6 +213,9 @@ int build_plan(const PlanInput& in, PlanResult* out, std::string* err) {
   };
   // Queues: queue_begin[q] .. queue_begin[q + 1] index the unit array.
   const bool fixed = (in.flags & kFlagGraphStable) != 0;
+  // Workgroups per CU the launch is planned (and, at D=64, built) for: three
+  // for D=64 batches of long units, by their mean key range times the group
+  // size (kPrefillLongUnitKeys).
   int wgs = decode ? kDecodeWgPerCu : prefill_wg_per_cu(in.head_dim);
   if (!decode && in.head_dim == 64 && !fixed && in.workers_override <= 0 && !in.qo_begin && !units.empty()) {
     int64_t keys = 0;
