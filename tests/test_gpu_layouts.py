@@ -81,3 +81,13 @@ def test_strided_rejects_bad_strides():
     with pytest.raises(pka.PkaError):
         plan.run_strided(w.q.to(dev), bad, bad)
     plan.close()
+
+
+def test_layouts_head_dim_64_three_per_cu():
+    """A D=64 batch of long units (three workgroups per CU, the build made
+    for three) through every layout."""
+    w = W.gqa_append(seed=79, batch=32, prefix_range=(2000, 4000), chunk_range=(16, 64), page_size=16, head_dim=64)
+    plan = _plan(w)
+    assert plan.info["num_workers"] > 2 * 256, plan.info["num_workers"]
+    plan.close()
+    _check_layouts(w, "D=64 three per CU")
